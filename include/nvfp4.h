@@ -1,0 +1,189 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 library: two-level NVFP4
+ * quantize / dequantize, the block-scaled W4A4 GEMM that consumes the
+ * quantized operands, a bf16 passthrough GEMM for layers kept in higher
+ * precision, and the layer predicate that chooses between the two.
+ *
+ * Sources.  The pages this library follows describe NVFP4 only in outline:
+ *   [P1] "英伟达B200狂飙10.2倍！AI绘图告别龟速！" (nmedialink.com), section
+ *        "NVFP4量化：在精度与速度之间寻得最佳平衡": two-level micro-block
+ *        scaling, an FP32 per-tensor scale (static or dynamic), a per-block
+ *        scale computed dynamically over blocks of 16 elements, the
+ *        exclude_pattern regex naming layers kept in higher precision, and
+ *        apply_visual_gen_linear(load_parameters, quantize_weights, ...).
+ *   [P2] "NVIDIA介绍用TensorRT LLM VisualGen加速Blackwell上的FLUX 3 Image
+ *        Klein" (sns.style), time-breakdown paragraph: NVFP4 weights in the
+ *        DiT linear layers; a tuned NVFP4 GEMM kernel.
+ *   [P3] "NVIDIA показала, как сократить генерацию FLUX 3 Image Klein с 22 до
+ *        6 секунд" (xalabuda.com), section "Квантование NVFP4 и оптимизация
+ *        вычислительных ядер": NVFP4 GEMM kernels for the linear layers.
+ * The element and scale encodings are those of the NVFP4 format: E2M1 4-bit
+ * elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; sign in bit 3), two per
+ * byte with the lower-indexed element in the low nibble, and one E4M3 (OCP
+ * "fn", max 448) byte per 16-element block.
+ *
+ * Conventions shared by every call:
+ *   - All tensors are row-major and contiguous.  A weight is [N, K] (the
+ *     nn.Linear layout), so a linear layer computes Y = X * W^T.
+ *   - Every pointer argument except `layer_name` and `pattern` is a DEVICE
+ *     pointer on the current HIP device.  The caller owns every buffer; the
+ *     library never allocates or frees memory and keeps no state beyond a
+ *     cached per-device architecture check.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on it and return without synchronizing.  Outputs are ready when the
+ *     stream reaches that point.
+ *   - Every call returns an nvfp4_status synchronously.  Checks run in the
+ *     order: null pointers -> shapes -> alignment -> workspace -> device ->
+ *     launch, and all argument checks happen before any HIP call, so a bad
+ *     argument is reported without touching the GPU.  A launch failure is
+ *     reported as NVFP4_ERR_HIP.  Data-dependent errors (Inf / NaN input) are
+ *     reported on the device through the optional `dev_status` word.
+ *   - Sizes are elements unless named *_bytes.  A zero row count is a no-op
+ *     that returns NVFP4_OK.
+ *   - Calls on one stream are ordered; calls that share output buffers on
+ *     different streams race.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+#define NVFP4_BLOCK 16 /* elements per block scale, [P1] "NVFP4量化" */
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = -1,      /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = -2,     /* negative size, or cols / K not a positive multiple of 16 */
+  NVFP4_ERR_ALIGN = -3,     /* a pointer misses its required alignment */
+  NVFP4_ERR_WORKSPACE = -4, /* workspace smaller than nvfp4_quantize_workspace_bytes() */
+  NVFP4_ERR_DEVICE = -5,    /* no HIP device, or the current device is not gfx950 */
+  NVFP4_ERR_ARG = -6,       /* unknown epilogue or other invalid argument */
+  NVFP4_ERR_HIP = -7,       /* a HIP launch or runtime call failed */
+  NVFP4_ERR_NONFINITE = -8  /* (device status word only) Inf or NaN in the input */
+} nvfp4_status;
+
+typedef enum {
+  NVFP4_EPI_NONE = 0, /* y = acc * sA * sW + bias */
+  NVFP4_EPI_GELU = 1  /* y = gelu_erf(acc * sA * sW + bias), gelu_erf(z) = z/2 (1 + erf(z/sqrt 2)) */
+} nvfp4_epilogue;
+
+/* NVFP4_ABI_VERSION of the loaded library. */
+int nvfp4_abi_version(void);
+
+/* Static, NUL-terminated text for a status code (never NULL). */
+const char* nvfp4_status_string(int status);
+
+/* Bytes of device workspace nvfp4_quantize needs for a [rows, cols] input when
+ * it computes the tensor amax itself (amax_in == NULL): 4 bytes per partial
+ * maximum, at most 4096 bytes.  0 when rows or cols is not positive. */
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * nvfp4_quantize -- two-level NVFP4 quantization of a bf16 tensor
+ * ([P1] "NVFP4量化": an FP32 per-tensor scale plus a scale computed
+ * dynamically for every block of 16 elements; here along each row).
+ *
+ *   x_bf16        [rows, cols] bf16, 16-byte aligned.
+ *   rows, cols    rows >= 0; cols > 0 and cols % 16 == 0.
+ *   codes         out [rows, cols/2] bytes: element 2j in the low nibble of
+ *                 byte j, element 2j+1 in the high nibble; 8-byte aligned.
+ *   scales        out [rows, cols/16] E4M3 bytes, row-major.
+ *   tensor_scale  out, 1 float: the stored FP32 per-tensor scale s_dec.
+ *   amax_in       NULL: the tensor amax = max|x| is computed here (uses
+ *                 `workspace`).  Non-NULL: 1 device float holding the amax
+ *                 as a producer computed it (the GEMM epilogue's y_amax);
+ *                 the input is then read once.
+ *   workspace     device scratch of at least nvfp4_quantize_workspace_bytes()
+ *                 bytes, 4-byte aligned, needed only when amax_in == NULL;
+ *                 contents on entry do not matter.
+ *   dev_status    optional device int32: written with NVFP4_OK, or
+ *                 NVFP4_ERR_NONFINITE when the amax is Inf / NaN, in which
+ *                 case *tensor_scale is set to NaN and codes / scales are
+ *                 left unspecified.
+ *
+ * The arithmetic, in binary32 round-to-nearest-even:
+ *   amax < 2^-96 (all-zero input included): s_enc = s_dec = 1, every scale 0.
+ *   otherwise s_enc = 2688 / amax, s_dec = 1 / s_enc      (2688 = 6 * 448)
+ *   per block b: a_b = max|x| over the block;  S_b = E4M3((a_b / 6) * s_enc),
+ *     nearest-even, saturating at 448;
+ *   S_b == 0: every code is its input's sign bit (code 8 for negatives);
+ *   else e_b = 1 / (S_b * s_dec), code = sign | E2M1(|x| * e_b), nearest-even,
+ *     saturating at 6.
+ * Deterministic: the same input gives the same bytes on every call.
+ */
+int nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols,
+                   uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                   const float* amax_in, void* workspace, size_t workspace_bytes,
+                   int32_t* dev_status, void* stream);
+
+/*
+ * nvfp4_dequantize -- NVFP4 back to bf16:
+ *   y = bf16_rne( (value(code) * S_b) * s_dec ), binary32 products.
+ * Code 8 (negative zero) gives -0.0.  Layouts as in nvfp4_quantize;
+ * y_bf16 [rows, cols] must be 16-byte aligned.
+ */
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
+                     const float* tensor_scale, int64_t rows, int64_t cols,
+                     void* y_bf16, void* stream);
+
+/*
+ * nvfp4_gemm -- block-scaled W4A4 GEMM of a DiT linear layer
+ * ([P2] time-breakdown paragraph; [P3] "Квантование NVFP4 ..."):
+ *
+ *   Y[m,n] = bf16_rne( epi( sA * sW * sum_k Ahat[m,k] * What[n,k] + bias[n] ) )
+ *
+ * with Ahat = value(codeA) * S_A[m, k/16] and What = value(codeW) *
+ * S_W[n, k/16] decoded exactly (each product of an E2M1 value and an E4M3
+ * scale is exact in fp16), fp32 accumulation, and the per-tensor scales
+ * sA = *a_tensor_scale, sW = *w_tensor_scale applied once in the epilogue.
+ *
+ *   a_codes/a_scales  [M, K/2] / [M, K/16] as written by nvfp4_quantize.
+ *   w_codes/w_scales  [N, K/2] / [N, K/16].
+ *   bias_bf16         optional [N] bf16.
+ *   M, N >= 0; K > 0, K % 16 == 0.  Code pointers 8-byte aligned.
+ *   epilogue          an nvfp4_epilogue value.
+ *   y_bf16            out [M, N] bf16, 4-byte aligned; N % 2 == 0 is not
+ *                     required.
+ *   y_amax            optional device float: set to max |Y| over the bf16
+ *                     outputs (the call zeroes it first, on `stream`), ready
+ *                     to be passed as amax_in of the next nvfp4_quantize.
+ */
+int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+               const uint8_t* w_codes, const uint8_t* w_scales, const float* w_tensor_scale,
+               const void* bias_bf16, int64_t M, int64_t N, int64_t K, int epilogue,
+               void* y_bf16, float* y_amax, void* stream);
+
+/*
+ * nvfp4_gemm_bf16 -- the bf16 passthrough for layers kept in higher precision
+ * ([P1] "NVFP4量化": chosen layers keep their original precision):
+ *   Y[m,n] = bf16_rne( epi( sum_k X[m,k] * W[n,k] + bias[n] ) ), fp32 accumulation.
+ *   x_bf16 [M, K], w_bf16 [N, K], bias_bf16 optional [N], y_bf16 [M, N];
+ *   M, N >= 0, K > 0, K % 8 == 0; x / w 16-byte aligned, y 4-byte aligned.
+ */
+int nvfp4_gemm_bf16(const void* x_bf16, const void* w_bf16, const void* bias_bf16,
+                    int64_t M, int64_t N, int64_t K, int epilogue, void* y_bf16,
+                    void* stream);
+
+/*
+ * nvfp4_layer_is_quantized -- the exclude-pattern predicate of [P1]
+ * "NVFP4量化".  Host only; touches no device.
+ *   layer_name  NUL-terminated module path, e.g. "transformer_blocks.0.attn.to_q".
+ *   pattern     NUL-terminated ECMAScript regex, or NULL for the page's
+ *               pattern ^(?!.*(embedder|norm_out|proj_out|to_add_out|to_added_qkv|stream)).*
+ * Returns 1 when the pattern matches a prefix of the name (the layer runs in
+ * NVFP4), 0 when it does not (the layer stays bf16), NVFP4_ERR_NULL for a NULL
+ * name, NVFP4_ERR_ARG for a pattern that does not compile.
+ */
+int nvfp4_layer_is_quantized(const char* layer_name, const char* pattern);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,96 @@
+// Device helpers shared by the gfx950 kernels of the NVFP4 library.
+//
+// Formats (NVFP4): E2M1 elements, sign in bit 3, magnitudes 0, .5, 1, 1.5, 2,
+// 3, 4, 6; E4M3 block scales (OCP "fn", bias 7, max 448 = 0x7E, subnormal
+// quantum 2^-9); bf16 = the top half of a binary32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 128-bit load marked non-temporal (last use of the data: stream it through).
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Largest |x| of the two bf16 halves of a word, as a 16-bit magnitude pattern.
+__device__ __forceinline__ u16x2 abs_halves(uint32_t w) {
+  return __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+}
+
+__device__ __forceinline__ u16x2 max_u16x2(u16x2 a, u16x2 b) {
+  return __builtin_elementwise_max(a, b);
+}
+
+// binary32 -> E4M3 byte for t >= 0: nearest, ties to the even byte, saturating
+// at 448.  Below 2^-6 the E4M3 grid is uniform with quantum 2^-9, so t * 512
+// (exact) rounded to an integer with the hardware's nearest-even rounding is
+// the byte (0..8; 8 is the smallest normal, 0x08).  From 2^-6 up, the binary32
+// significand is rounded to 3 bits, nearest-even, by integer arithmetic, and
+// the exponent is rebiased from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_from_f32_rne(float t) {
+  if (t < 0.015625f) return (uint32_t)__builtin_rintf(t * 512.0f);
+  uint32_t u = __float_as_uint(t);
+  uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  uint32_t byte = ((((r >> 23) - 127u + 7u)) << 3) | ((r >> 20) & 7u);
+  return byte > 0x7Eu ? 0x7Eu : byte;
+}
+
+// E4M3 byte (0x00..0x7E) -> exact binary32.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  uint32_t e = b >> 3, m = b & 7u;
+  return e == 0 ? (float)m * 0.001953125f                     // m * 2^-9, exact
+                : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// binary32 -> bf16 bits, nearest-even (finite input; overflow gives Inf).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Two binary32 values -> two E2M1 codes in byte `sel` of `old`, element `a`
+// in the low nibble.  The gfx950 conversion rounds to nearest-even, saturates
+// at 6 and keeps the sign of zero; with scale 1.0 it applies no scaling.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Byte `SEL` of `w` (two E2M1 codes) -> two fp16 E2M1 values, exact.  The
+// conversion's scale operand only contributes its exponent; 1.0 adds nothing.
+template <int SEL>
+__device__ __forceinline__ f16x2 e2m1_unpack2_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1_unpack2_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,31 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Upper bound on the partial maxima the amax pass writes (workspace words).
+static constexpr int kMaxAmaxPartials = 1024;
+
+int amax_partial_count(int64_t numel);
+
+hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, float* tensor_scale, const float* amax_in,
+                           uint32_t* workspace, int32_t* dev_status, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales,
+                             const float* tensor_scale, int64_t rows, int64_t cols, void* y,
+                             hipStream_t stream);
+
+hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales,
+                             const float* a_tensor_scale, const uint8_t* w_codes,
+                             const uint8_t* w_scales, const float* w_tensor_scale,
+                             const void* bias, int64_t M, int64_t N, int64_t K, int epilogue,
+                             void* y, float* y_amax, hipStream_t stream);
+
+hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, int64_t M, int64_t N,
+                            int64_t K, int epilogue, void* y, hipStream_t stream);
+
+}  // namespace nvfp4

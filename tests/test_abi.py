@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/nvfp4.h declares, and reports argument errors synchronously before
+touching a device.  Fake device pointers are plain integers that are never
+dereferenced: every call here fails validation first (or fails the device
+check on a machine without a gfx950)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_block_scaled_05_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+OK, NULL, SHAPE, ALIGN, WORKSPACE, DEVICE, ARG = 0, -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_binding.LIB_PATH):
+        from nvfp4_block_scaled_05_amd import build
+        build.build()
+    return _binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _binding.SIGNATURES, n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.nvfp4_abi_version() == 1
+    for code in range(-8, 1):
+        assert lib.nvfp4_status_string(code)
+    assert lib.nvfp4_status_string(-99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert lib.nvfp4_quantize_workspace_bytes(0, 16) == 0
+    assert lib.nvfp4_quantize_workspace_bytes(-1, 16) == 0
+    small = lib.nvfp4_quantize_workspace_bytes(1, 16)
+    big = lib.nvfp4_quantize_workspace_bytes(16896, 3072)
+    assert 4 <= small <= big <= 4096 and big % 4 == 0
+
+
+A = 1 << 20        # fake, 16-byte aligned, never dereferenced
+S = 64
+
+
+def q(lib, x=A, rows=4, cols=32, codes=A, scales=A, ts=A, amax=None, ws=A, wsb=4096, st=None):
+    return lib.nvfp4_quantize(x, rows, cols, codes, scales, ts, amax, ws, wsb, st, None)
+
+
+def test_quantize_argument_errors(lib):
+    assert q(lib, x=None) == NULL
+    assert q(lib, ts=None) == NULL
+    assert q(lib, ws=None) == NULL                  # computing amax needs the workspace
+    assert q(lib, rows=-1) == SHAPE
+    assert q(lib, cols=24) == SHAPE
+    assert q(lib, cols=0) == SHAPE
+    assert q(lib, x=A + 8) == ALIGN
+    assert q(lib, codes=A + 4) == ALIGN
+    assert q(lib, ts=A + 2) == ALIGN
+    assert q(lib, wsb=0) == WORKSPACE
+    # workspace not needed when the producer's amax is given
+    assert q(lib, ws=None, wsb=0, amax=A) in (OK, DEVICE)
+
+
+def test_quantize_valid_args_reach_device_check(lib):
+    r = q(lib)
+    assert r in (DEVICE, OK)
+    if not _has_gfx950():
+        assert r == DEVICE
+
+
+def test_dequantize_argument_errors(lib):
+    d = lib.nvfp4_dequantize
+    assert d(None, A, A, 4, 32, A, None) == NULL
+    assert d(A, A, A, 4, 20, A, None) == SHAPE
+    assert d(A, A, A, 4, 32, A + 8, None) == ALIGN
+    assert d(A + 4, A, A, 4, 32, A, None) == ALIGN
+
+
+def g(lib, M=64, N=64, K=64, epi=0, y=A, bias=None, amax=None, ac=A, wc=A):
+    return lib.nvfp4_gemm(ac, A, A, wc, A, A, bias, M, N, K, epi, y, amax, None)
+
+
+def test_gemm_argument_errors(lib):
+    assert g(lib, y=None) == NULL
+    assert g(lib, K=40) == SHAPE
+    assert g(lib, K=0) == SHAPE
+    assert g(lib, M=-3) == SHAPE
+    assert g(lib, ac=A + 4) == ALIGN
+    assert g(lib, y=A + 1) == ALIGN
+    assert g(lib, amax=A + 2) == ALIGN
+    assert g(lib, epi=7) == ARG
+    b = lib.nvfp4_gemm_bf16
+    assert b(None, A, None, 8, 8, 64, 0, A, None) == NULL
+    assert b(A, A, None, 8, 8, 12, 0, A, None) == SHAPE
+    assert b(A + 8, A, None, 8, 8, 64, 0, A, None) == ALIGN
+    assert b(A, A, None, 8, 8, 64, 3, A, None) == ARG
+
+
+def test_layer_predicate_matches_python_re(lib):
+    from tests.test_oracle_layers import load_golden   # hand-written list
+    for name, want in load_golden():
+        assert lib.nvfp4_layer_is_quantized(name.encode(), None) == int(want), name
+    assert lib.nvfp4_layer_is_quantized(None, None) == NULL
+    assert lib.nvfp4_layer_is_quantized(b"abc", b"(unclosed") == ARG
+    assert lib.nvfp4_layer_is_quantized(b"blocks.1.ff", b"blocks") == 1
+    assert lib.nvfp4_layer_is_quantized(b"x.blocks", b"blocks") == 0   # match at the start only
+
+
+def _has_gfx950():
+    try:
+        import torch
+        return torch.cuda.is_available() and "gfx950" in torch.cuda.get_device_properties(0).gcnArchName
+    except Exception:
+        return False

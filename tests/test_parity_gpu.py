@@ -1,0 +1,370 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+  * quantize: codes, scales and the FP32 tensor scale bit-exact, on the DiT
+    workload shapes at full size, ragged shapes, and adversarial tensors;
+  * dequantize: bf16 output bit-exact;
+  * block-scaled GEMM: relative Frobenius error <= 2e-3 against the oracle's
+    exact sum rounded to bf16 (the acceptance bar), with the share of outputs
+    more than one bf16 ulp away reported and bounded;
+  * epilogues (bias, GELU, output amax), the MLP chain stage by stage, and the
+    bf16 passthrough.
+Inputs are the seeded generators of nvfp4_block_scaled_05_amd.inputs; the
+oracle always quantizes its own copy of the inputs.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+
+import nvfp4_block_scaled_05_amd as nv
+from nvfp4_block_scaled_05_amd import inputs as W
+from oracle import (bf16_bits_to_f32, dequantize as o_dequantize, gemm_fp64,
+                    gemm_exact_rows, linear_bf16_fp64, quantize as o_quantize)
+from tests.gpu_util import bits_of, f32_dev, rel_frobenius, to_dev, ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+GEMM_TOL = 2e-3          # relative Frobenius error bound of the block-scaled GEMM
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    nv.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def gpu_quantize(bits, amax=None):
+    q = nv.quantize(to_dev(bits), amax=None if amax is None else f32_dev(amax))
+    _sync()
+    return q
+
+
+def assert_quant_equal(q, ref, label=""):
+    codes = q.codes.cpu().numpy()
+    scales = q.scales.cpu().numpy()
+    ts = q.tensor_scale.cpu().numpy()
+    bad_s = np.argwhere(scales != ref.scales)
+    assert len(bad_s) == 0, f"{label}: {len(bad_s)} scale mismatches, first {bad_s[:3]}"
+    bad_c = np.argwhere(codes != ref.codes)
+    assert len(bad_c) == 0, f"{label}: {len(bad_c)} code mismatches, first {bad_c[:3]}"
+    assert ts.view(np.uint32)[0] == np.float32(ref.tensor_scale).view(np.uint32), label
+
+
+def check_quantize(bits, amax=None, label=""):
+    q = gpu_quantize(bits, amax)
+    ref = o_quantize(bits, amax=amax)
+    assert_quant_equal(q, ref, label)
+    return q, ref
+
+
+# ----------------------------------------------------------------- quantize --
+
+SHAPES = [(1, 16), (3, 48), (37, 1040), (257, 3072), (5, 12288)]
+
+
+KINDS = ["normal", "t3", "outliers"]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("kind", KINDS)
+def test_quantize_ragged_shapes(shape, kind):
+    bits = W.random_matrix(1000 * SHAPES.index(shape) + KINDS.index(kind), shape, kind)
+    q, ref = check_quantize(bits, label=f"{shape} {kind}")
+    y = nv.dequantize(q)
+    _sync()
+    assert np.array_equal(bits_of(y), o_dequantize(ref.codes, ref.scales, ref.tensor_scale, shape[1]))
+
+
+def test_quantize_linear_small_workload():
+    d = W.linear_small()
+    check_quantize(d["x"], label="X [128,1024]")
+    check_quantize(d["w"], label="W [1024,1024]")
+
+
+def test_quantize_activation_full_size():
+    # 16896 x 3072, N(0,1) with 0.1% outliers x50: full tensor bit-exact, and
+    # the bf16 round trip bit-exact
+    bits = W.quantize_act()["x"]
+    q, ref = check_quantize(bits, label="act [16896,3072]")
+    y = nv.dequantize(q)
+    _sync()
+    assert np.array_equal(bits_of(y), o_dequantize(ref.codes, ref.scales, ref.tensor_scale, 3072))
+
+
+@functools.lru_cache(maxsize=None)
+def _mlp():
+    return W.mlp_2048()
+
+
+def test_quantize_student_t_full_size():
+    bits = _mlp()["x"]
+    check_quantize(bits, label="mlp X t(3)")
+
+
+def _adversarial(seed=0):
+    rng = np.random.default_rng(seed)
+    rows, cols = 64, 256
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[0, :16] = 0.0                                  # all-zero block
+    x[0, 16:32] = -0.0                               # negative zeros
+    x[1, :16] = 3.0                                  # constant block
+    x[2, :16] = x[2, :16] / np.abs(x[2, :16]).max() * np.float32(0.05)   # subnormal E4M3 scale
+    x[3, :16] = x[3, :16] * 3e-8                     # scale rounds to 0
+    x[4, :] = np.float32(1e-39) * np.sign(x[4, :])   # bf16 subnormals
+    x[5, 7] = 3000.0                                 # one huge outlier (the tensor max)
+    for j in range(16):                              # tensor max in every block position
+        x[6 + j, 16 * (j % 16) + j] = -2999.0
+    return W.f32_to_bf16_bits(x)
+
+
+def test_quantize_adversarial():
+    bits = _adversarial()
+    q, ref = check_quantize(bits, label="adversarial")
+    y = nv.dequantize(q)
+    _sync()
+    assert np.array_equal(bits_of(y), o_dequantize(ref.codes, ref.scales, ref.tensor_scale, 256))
+    assert (ref.scales == 0).any() and ((ref.scales > 0) & (ref.scales < 8)).any()
+
+
+def test_quantize_exact_e2m1_ties():
+    # amax = 2688 makes s_enc = s_dec = 1; a block with max 6 gets scale 1.0, so
+    # the elements reach the E2M1 encoder unscaled and sit exactly on its ties
+    x = np.zeros((4, 32), np.float32)
+    x[0, 0] = 2688.0
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    x[1, :8], x[1, 8:16] = ties, -ties
+    x[2, :16] = np.array([6.0, 0.2, 0.3, 0.7, 0.8, 1.2, 1.3, 1.7, 1.8, 2.4, 2.6, 3.4, 3.6, 4.9, 5.1, 7.0],
+                         np.float32)
+    bits = W.f32_to_bf16_bits(x)
+    q, ref = check_quantize(bits, label="ties")
+    assert ref.tensor_scale == np.float32(1.0) and ref.scales[1, 0] == 0x38   # 1.0
+
+
+def test_quantize_degenerate():
+    for fill in (0.0, -0.0, 1e-38):
+        bits = W.f32_to_bf16_bits(np.full((4, 32), fill, np.float32))
+        check_quantize(bits, label=f"fill {fill}")
+
+
+def test_quantize_with_producer_amax():
+    bits = W.random_matrix(3, (96, 640), "t3")
+    amax = np.abs(bf16_bits_to_f32(bits)).max()
+    check_quantize(bits, amax=amax, label="amax given")
+    check_quantize(bits, amax=np.float32(amax * 3.0), label="amax larger")
+
+
+def test_quantize_nonfinite_reports_status():
+    import torch
+    for bad in (np.inf, -np.inf, np.nan):
+        x = np.ones((8, 64), np.float32)
+        x[5, 9] = bad
+        status = torch.full((1,), 123, dtype=torch.int32, device="cuda")
+        q = nv.quantize(to_dev(W.f32_to_bf16_bits(x)), dev_status=status)
+        _sync()
+        assert int(status.item()) == -8
+        assert np.isnan(q.tensor_scale.item())
+    status = torch.full((1,), 123, dtype=torch.int32, device="cuda")
+    nv.quantize(to_dev(W.random_matrix(1, (8, 64))), dev_status=status)
+    _sync()
+    assert int(status.item()) == 0
+
+
+def test_quantize_empty_rows():
+    import torch
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q = nv.quantize(x)
+    _sync()
+    assert q.codes.shape == (0, 32)
+
+
+def test_quantize_deterministic():
+    bits = W.random_matrix(9, (1000, 3072), "outliers")
+    x = to_dev(bits)
+    a = nv.quantize(x)
+    b = nv.quantize(x)
+    _sync()
+    assert np.array_equal(a.codes.cpu().numpy(), b.codes.cpu().numpy())
+    assert np.array_equal(a.scales.cpu().numpy(), b.scales.cpu().numpy())
+
+
+# --------------------------------------------------------------------- GEMM --
+
+def _gemm_case(M, N, K, seed, kind_a="t3", bias=False, epilogue="none"):
+    a_bits = W.random_matrix(seed, (M, K), kind_a)
+    w_bits = W.random_matrix(seed + 1, (N, K), "normal", 0.02)
+    b_bits = W.random_matrix(seed + 2, (1, N), "normal", 0.1)[0] if bias else None
+    qa, ra = check_quantize(a_bits, label="A")
+    qw, rw = check_quantize(w_bits, label="W")
+    y = nv.gemm(qa, qw, bias=None if b_bits is None else to_dev(b_bits), epilogue=epilogue)
+    _sync()
+    ref, _ = gemm_fp64(ra, rw, K, bias_bits=b_bits, gelu=epilogue == "gelu")
+    return bits_of(y), ref
+
+
+def assert_gemm_close(y, ref, label=""):
+    err = rel_frobenius(y, ref)
+    ulps = ulp_diff(y, ref)
+    far = float((ulps > 1).mean())
+    assert err <= GEMM_TOL, f"{label}: rel Frobenius {err:.3e}"
+    assert far <= 1e-2, f"{label}: {far:.2e} of outputs more than 1 ulp away"
+    return err
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (130, 70, 48), (256, 384, 1024),
+                                   (200, 300, 3088), (1, 129, 16), (129, 1, 256)])
+def test_gemm_small_and_ragged(M, N, K):
+    y, ref = _gemm_case(M, N, K, seed=M * 7 + N + K)
+    assert_gemm_close(y, ref, f"{M}x{N}x{K}")
+
+
+def test_gemm_bias_and_gelu():
+    y, ref = _gemm_case(192, 256, 512, seed=5, bias=True, epilogue="gelu")
+    assert_gemm_close(y, ref, "bias+gelu")
+    y, ref = _gemm_case(192, 256, 512, seed=6, bias=True)
+    assert_gemm_close(y, ref, "bias")
+
+
+def test_gemm_linear_small_workload():
+    # X [128,1024], W [1024,1024]: both dynamically quantized, full comparison
+    d = W.linear_small()
+    qa, ra = check_quantize(d["x"])
+    qw, rw = check_quantize(d["w"])
+    y = nv.gemm(qa, qw)
+    _sync()
+    ref, _ = gemm_fp64(ra, rw, 1024)
+    assert_gemm_close(bits_of(y), ref, "linear 128x1024x1024")
+
+
+def test_gemm_exact_sum_sampled_rows():
+    # the float64 oracle agrees with the exact int64 form on these rows too
+    M, N, K = 300, 512, 3072
+    a_bits = W.random_matrix(41, (M, K), "t3")
+    w_bits = W.random_matrix(42, (N, K), "normal", 0.02)
+    qa, ra = check_quantize(a_bits)
+    qw, rw = check_quantize(w_bits)
+    y = bits_of(nv.gemm(qa, qw))
+    rows = np.arange(0, M, 7)
+    ref, _ = gemm_exact_rows(ra, rw, K, rows)
+    assert_gemm_close(y[rows], ref, "exact rows")
+
+
+@functools.lru_cache(maxsize=None)
+def _oracle_weight(name, seed=0):
+    bits = W.qkv_1024(seed)["w"] if name == "qkv" else _mlp()[name]
+    return bits, o_quantize(bits)
+
+
+def _sampled_rows(M, n=96, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, n, replace=False)]))
+
+
+def test_gemm_qkv_1024_sampled_rows():
+    # X [4608,3072] quantized per call, W [9216,3072] pre-quantized
+    x_bits = W.qkv_1024()["x"]
+    w_bits, rw = _oracle_weight("qkv")
+    qx = gpu_quantize(x_bits)
+    qw = gpu_quantize(w_bits)
+    y = bits_of(nv.gemm(qx, qw))
+    rows = _sampled_rows(4608)
+    amax = np.abs(bf16_bits_to_f32(x_bits)).max()
+    rx = o_quantize(x_bits[rows], amax=amax)          # the rows of the full-tensor quantization
+    assert_quant_equal(qw, rw, "W qkv")
+    ref, _ = gemm_fp64(rx, rw, 3072)
+    assert_gemm_close(y[rows], ref, "qkv sampled rows")
+
+
+def test_mlp_2048_chain_stage_by_stage():
+    import torch
+    x_bits = _mlp()["x"]
+    wu_bits, rwu = _oracle_weight("w_up")
+    wd_bits, rwd = _oracle_weight("w_down")
+    qwu, qwd = gpu_quantize(wu_bits), gpu_quantize(wd_bits)
+    assert_quant_equal(qwu, rwu, "W_up")
+    assert_quant_equal(qwd, rwd, "W_down")
+    qx = gpu_quantize(x_bits)
+    amax = torch.empty((1,), dtype=torch.float32, device="cuda")
+    h = nv.gemm(qx, qwu, epilogue="gelu", y_amax=amax)
+    qh = nv.quantize(h, amax=amax)
+    y = nv.gemm(qh, qwd)
+    _sync()
+    rows = _sampled_rows(16896, n=48)
+    # stage 1: H = GELU(Xq @ Wup^T) on sampled rows
+    x_amax = np.abs(bf16_bits_to_f32(x_bits)).max()
+    rx = o_quantize(x_bits[rows], amax=x_amax)
+    h_ref, _ = gemm_fp64(rx, rwu, 3072, gelu=True)
+    h_bits = bits_of(h)
+    assert_gemm_close(h_bits[rows], h_ref, "up+gelu")
+    # stage 2: the epilogue amax is max |H_gpu| exactly
+    h_amax = np.abs(bf16_bits_to_f32(h_bits)).max()
+    assert np.float32(amax.item()) == np.float32(h_amax)
+    # stage 3: quantize(H_gpu) bit-exact on the sampled rows (amax is global)
+    rh = o_quantize(h_bits[rows], amax=h_amax)
+    assert np.array_equal(qh.codes.cpu().numpy()[rows], rh.codes)
+    assert np.array_equal(qh.scales.cpu().numpy()[rows], rh.scales)
+    assert np.float32(qh.tensor_scale.item()) == rh.tensor_scale
+    # stage 4: Y = Hq @ Wdown^T on the sampled rows
+    y_ref, _ = gemm_fp64(rh, rwd, 12288)
+    assert_gemm_close(bits_of(y)[rows], y_ref, "down")
+
+
+def test_gemm_amax_epilogue_exact():
+    import torch
+    a_bits = W.random_matrix(61, (333, 512), "t3")
+    w_bits = W.random_matrix(62, (250, 512), "normal", 0.02)
+    qa, qw = gpu_quantize(a_bits), gpu_quantize(w_bits)
+    amax = torch.full((1,), 1e30, dtype=torch.float32, device="cuda")   # zeroed by the call
+    y = nv.gemm(qa, qw, y_amax=amax)
+    _sync()
+    assert np.float32(amax.item()) == np.abs(bf16_bits_to_f32(bits_of(y))).max()
+
+
+def test_gemm_deterministic():
+    a_bits = W.random_matrix(71, (512, 1024), "t3")
+    w_bits = W.random_matrix(72, (768, 1024), "normal", 0.02)
+    qa, qw = gpu_quantize(a_bits), gpu_quantize(w_bits)
+    y1, y2 = bits_of(nv.gemm(qa, qw)), bits_of(nv.gemm(qa, qw))
+    assert np.array_equal(y1, y2)
+
+
+# ------------------------------------------------------- bf16 passthrough --
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (130, 70, 40), (2, 1000, 3072), (300, 257, 1024)])
+def test_gemm_bf16(M, N, K):
+    x = W.random_matrix(M + N, (M, K), "normal")
+    w = W.random_matrix(M + N + 1, (N, K), "normal", 0.02)
+    b = W.random_matrix(M + N + 2, (1, N), "normal", 0.1)[0]
+    y = bits_of(nv.gemm_bf16(to_dev(x), to_dev(w), bias=to_dev(b)))
+    ref = linear_bf16_fp64(x, w, b)
+    assert_gemm_close(y, ref, f"bf16 {M}x{N}x{K}")
+
+
+def test_gemm_bf16_modulation_shape():
+    # a modulation linear kept bf16: temb [2,3072] x W [18432,3072]
+    temb = W.random_matrix(81, (2, 3072), "normal")
+    w_mod = W.random_matrix(82, (18432, 3072), "normal", 0.02)
+    y = bits_of(nv.gemm_bf16(to_dev(temb), to_dev(w_mod)))
+    ref = linear_bf16_fp64(temb, w_mod)
+    assert_gemm_close(y, ref, "modulation [2,3072]x[18432,3072]")
+
+
+def test_linear_dispatch_by_layer_name():
+    d = W.linear_small()
+    x = to_dev(d["x"])
+    wq = nv.quantize_weight(to_dev(d["w"]))
+    y_q = bits_of(nv.linear(x, wq, "transformer_blocks.0.attn.to_q"))
+    ra, rw = o_quantize(d["x"]), o_quantize(d["w"])
+    ref, _ = gemm_fp64(ra, rw, 1024)
+    assert_gemm_close(y_q, ref, "nvfp4 layer")
+    y_b = bits_of(nv.linear(x, to_dev(d["w"]), "proj_out"))
+    assert_gemm_close(y_b, linear_bf16_fp64(d["x"], d["w"]), "bf16 layer")
