@@ -1,0 +1,289 @@
+"""Throughput of the NVFP4 DiT-linear hot path on one MI355X.
+
+One step = the DiT MLP at 2048x2048 (16384 image + 512 text tokens, hidden
+3072, MLP 12288) as an NVFP4 model runs it:
+
+    quantize(X)                      amax pass + block quantizer   (X bf16 [16896,3072])
+    H = gemm(Xq, Wup_q, GELU, amax)  block-scaled W4A4 GEMM         (16896 x 12288 x 3072)
+    quantize(H, amax)                single-pass quantizer          (H bf16 [16896,12288])
+    Y = gemm(Hq, Wdown_q)            block-scaled W4A4 GEMM         (16896 x 3072 x 12288)
+
+The weights are quantized once before timing (load-time weight quantization),
+and their quantization is timed separately.  `value` is the two GEMMs' FLOPs
+(2*M*N*K each) over the whole step's time, in TFLOP/s.  The JSON line also
+carries the per-stage times, the roofline of the dominant kernel (the up
+GEMM, timed with HIP events on the stream it runs on), the standalone
+quantize / dequantize rates on the [16896,3072] activation with caches
+flushed, the bf16 passthrough on a modulation-shaped layer, and the CPU
+oracle timed on a row sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --calib-copy     (plain 1 GiB device copy, for counter calibration)
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+TOKENS, HIDDEN, MLP = 16896, 3072, 12288
+GEMM_FLOP = 2 * TOKENS * MLP * HIDDEN              # each of up and down
+PEAK_MFMA_F16 = 2500.0                              # TFLOP/s, dense fp16/bf16 MFMA
+PEAK_HBM = 8000.0                                   # GB/s
+QUANT_BYTES_PER_ELEM = 2 + 0.5 + 1.0 / 16           # bf16 read + codes + scales
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-rows", type=int, default=192)
+    p.add_argument("--calib-copy", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "nvfp4_block_scaled_05_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, launches_per_step):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards along tokens with no communication inside a layer; "
+              "see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import nvfp4_block_scaled_05_amd as nv
+    from nvfp4_block_scaled_05_amd import inputs
+
+    if args.calib_copy:
+        n = 1 << 30
+        a = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n}))
+        return
+
+    nv.load()
+    dev = "cuda"
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------------------------------------------------------- setup --
+    t0 = time.time()
+    data = inputs.mlp_2048()
+    x = to_dev(data["x"])
+    w_up, w_down = to_dev(data["w_up"]), to_dev(data["w_down"])
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # weight pre-quantization (load time), timed separately
+    wq_up = nv.quantize_weight(w_up)
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    wq_up = nv.quantize_weight(w_up)
+    e1.record(stream)
+    wq_down = nv.quantize_weight(w_down)
+    torch.cuda.synchronize()
+    wquant_us = e0.elapsed_time(e1) * 1e3
+
+    # preallocated step buffers
+    ws = torch.empty(nv.quantize_workspace_bytes(TOKENS, HIDDEN), dtype=torch.uint8, device=dev)
+    xq = nv.quantize(x, workspace=ws)
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    h = nv.gemm(xq, wq_up, epilogue="gelu", y_amax=amax)
+    hq = nv.quantize(h, amax=amax)
+    y = nv.gemm(hq, wq_down)
+    xq_out = (xq.codes, xq.scales, xq.tensor_scale)
+    hq_out = (hq.codes, hq.scales, hq.tensor_scale)
+
+    stage_names = ["quantize_x", "gemm_up_gelu_amax", "quantize_h", "gemm_down"]
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        nv.quantize(x, workspace=ws, out=xq_out)
+        if events is not None:
+            events[1].record(stream)
+        nv.gemm(xq, wq_up, epilogue="gelu", y_amax=amax, out=h)
+        if events is not None:
+            events[2].record(stream)
+        nv.quantize(h, amax=amax, out=hq_out)
+        if events is not None:
+            events[3].record(stream)
+        nv.gemm(hq, wq_down, out=y)
+        if events is not None:
+            events[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev_sets = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(ev_sets[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    stage_us = {n: float(np.mean([s[j].elapsed_time(s[j + 1]) * 1e3 for s in ev_sets]))
+                for j, n in enumerate(stage_names)}
+    value = 2 * GEMM_FLOP / (ms_per_step * 1e-3) / 1e12
+
+    # roofline of the dominant kernel: the up GEMM
+    up_us = stage_us["gemm_up_gelu_amax"]
+    achieved = GEMM_FLOP / (up_us * 1e-6) / 1e12
+    traffic = measured_traffic("gemm_nvfp4_kernel", 2)
+    roofline = {"kernel": "gemm_nvfp4_kernel (up, GELU + amax epilogue)", "bound": "mfma",
+                "achieved": round(achieved, 1), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_MFMA_F16, 4), "traffic": traffic,
+                "algorithmic_flop_per_launch": GEMM_FLOP, "avg_launch_us": round(up_us, 2)}
+
+    # ------------------------------------- standalone quantize / dequantize --
+    act = to_dev(inputs.quantize_act()["x"])
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    ws2 = torch.empty(nv.quantize_workspace_bytes(TOKENS, HIDDEN), dtype=torch.uint8, device=dev)
+    qa = nv.quantize(act, workspace=ws2)
+    qa_out = (qa.codes, qa.scales, qa.tensor_scale)
+    y_act = torch.empty_like(act)
+
+    def timed(fn, iters=20, flush_first=True):
+        ts = []
+        for _ in range(3):
+            fn()
+        for _ in range(iters):
+            if flush_first:
+                flush.fill_(0.0)
+            a, b = ev(), ev()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return float(np.median(ts))
+
+    n_act = TOKENS * HIDDEN
+    q_us = timed(lambda: nv.quantize(act, workspace=ws2, out=qa_out))
+    q_warm_us = timed(lambda: nv.quantize(act, workspace=ws2, out=qa_out), flush_first=False)
+    dq_us = timed(lambda: nv.dequantize(qa, out=y_act))
+    q_bytes = n_act * QUANT_BYTES_PER_ELEM
+    quant = {"workload": "activation [16896,3072] N(0,1) + 0.1% outliers x50",
+             "quantize_us": round(q_us, 2), "quantize_GBps": round(q_bytes / q_us / 1e3, 1),
+             "quantize_frac_hbm": round(q_bytes / q_us / 1e3 / PEAK_HBM, 4),
+             "quantize_warm_us": round(q_warm_us, 2),
+             "dequantize_us": round(dq_us, 2), "dequantize_GBps": round(q_bytes / dq_us / 1e3, 1),
+             "algorithmic_bytes": int(q_bytes), "caches": "512 MiB flush before each launch"}
+    h_bytes = TOKENS * MLP * QUANT_BYTES_PER_ELEM
+    quant["quantize_h_in_step_GBps"] = round(h_bytes / stage_us["quantize_h"] / 1e3, 1)
+
+    # bf16 passthrough on a modulation-shaped layer kept high precision
+    temb = to_dev(inputs.random_matrix(81, (2, HIDDEN)))
+    w_mod = to_dev(inputs.random_matrix(82, (6 * HIDDEN, HIDDEN), std=0.02))
+    ymod = nv.gemm_bf16(temb, w_mod)
+    mod_us = timed(lambda: nv.gemm_bf16(temb, w_mod, out=ymod), iters=10)
+    bf16_pass = {"layer": "modulation [2,3072] x [18432,3072]^T (bf16 by the exclude pattern)",
+                 "selected_bf16": not nv.layer_is_quantized("blocks.0.double_stream_modulation.lin"),
+                 "us": round(mod_us, 2),
+                 "GBps_weight_read": round(6 * HIDDEN * HIDDEN * 2 / mod_us / 1e3, 1)}
+    del flush
+
+    # ----------------------------------------------------------- CPU oracle --
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(data, args.cpu_rows)
+
+    rec = {
+        "metric": "NVFP4 GEMM TFLOP/s + quantize HBM GB/s on DiT linear shapes (% of peak)",
+        "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4 e2m1/e4m3 operands, exact f16 decode, f16 MFMA, f32 accumulate, bf16 out",
+        "data": "synthetic (seeded: X Student-t(3), W 0.02*N(0,1))",
+        "config": {"workload": "dit_mlp_2048: quantize X -> GEMM up + GELU + amax -> "
+                               "quantize H -> GEMM down",
+                   "tokens": TOKENS, "hidden": HIDDEN, "mlp": MLP,
+                   "flop_per_step": 2 * GEMM_FLOP, "parallelism": "single GPU"},
+        "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "weight_quantize_us": round(wquant_us, 2),
+        "roofline": roofline,
+        "quantize": quant,
+        "bf16_passthrough": bf16_pass,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(rec))
+
+
+def cpu_baseline(data, rows):
+    """The CPU oracle, untuned, on a row sample of the same step."""
+    import oracle
+    from oracle.formats import bf16_bits_to_f32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    rng = np.random.default_rng(0)
+    sel = np.sort(rng.choice(TOKENS, rows, replace=False))
+    x = data["x"]
+    t_w = time.perf_counter()
+    rwu = oracle.quantize(data["w_up"])
+    rwd = oracle.quantize(data["w_down"])
+    t_w = time.perf_counter() - t_w
+    t0 = time.perf_counter()
+    amax = np.abs(bf16_bits_to_f32(x)).max()
+    rx = oracle.quantize(x[sel], amax=amax)
+    h_bits, _ = oracle.gemm_fp64(rx, rwu, HIDDEN, gelu=True)
+    h_amax = np.abs(bf16_bits_to_f32(h_bits)).max()
+    rh = oracle.quantize(h_bits, amax=h_amax)
+    oracle.gemm_fp64(rh, rwd, MLP)
+    dt = time.perf_counter() - t0
+    flop = 2 * 2 * rows * MLP * HIDDEN
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows} of {TOKENS} token rows through the whole step (amax over all of X, "
+                      f"quantize, float64-BLAS GEMM up + GELU, quantize H, GEMM down); "
+                      f"weights quantized beforehand in {t_w:.1f}s (not counted)",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

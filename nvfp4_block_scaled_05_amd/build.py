@@ -17,6 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libnvfp4.so")
+PROBE_LIB = os.path.join(LIBDIR, "libnvfp4_isa_probe.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -32,7 +33,8 @@ DEVICE_FLAGS = [
 ]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-I", INCLUDE, "-Wall"]
 
-SOURCES = ["quantize.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm_nvfp4.hip", "gemm.hip", "api.cpp"]
+PROBE_SOURCES = ["isa_probe.hip"]     # test-only library of conversion probes
 
 
 def _compile(src):
@@ -53,19 +55,25 @@ def build(verbose=False):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(OBJDIR, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        results = list(ex.map(_compile, SOURCES))
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(5, len(srcs))) as ex:
+        results = dict(zip(srcs, ex.map(_compile, srcs)))
     if verbose:
-        for (_, out), src in zip(results, SOURCES):
+        for src, (_, out) in results.items():
             if out:
                 print(f"[{src}]\n{out}")
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+    _link(LIB, [results[s][0] for s in SOURCES])
+    _link(PROBE_LIB, [results[s][0] for s in PROBE_SOURCES])
+    return LIB
+
+
+def _link(target, objs):
+    tmp = target + f".tmp{os.getpid()}"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
 
 
 def clean():

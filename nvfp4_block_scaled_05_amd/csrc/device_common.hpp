@@ -17,6 +17,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 128-bit load marked non-temporal (last use of the data: stream it through).
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
@@ -47,7 +48,7 @@ __device__ __forceinline__ uint32_t e4m3_from_f32_rne(float t) {
   return byte > 0x7Eu ? 0x7Eu : byte;
 }
 
-// E4M3 byte (0x00..0x7E) -> exact binary32.
+// E4M3 scale byte (0x00..0x7E: non-negative, finite) -> exact binary32.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   uint32_t e = b >> 3, m = b & 7u;
   return e == 0 ? (float)m * 0.001953125f                     // m * 2^-9, exact
@@ -79,9 +80,33 @@ __device__ __forceinline__ f16x2 e2m1_unpack2_f16(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
 }
 
+// Two E4M3 bytes of `w` (bytes 0,1 or, with HI, bytes 2,3) -> two fp16, exact
+// (every finite E4M3 value, subnormals included, is an fp16 normal or zero).
+// The gfx950 conversion reads OCP E4M3; scale 1.0 adds nothing.
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3_pair_to_f16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
 template <int SEL>
 __device__ __forceinline__ f32x2 e2m1_unpack2_f32(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// 8 E2M1 codes (one dword, element 0 in the low nibble) times their block
+// scale s (one fp16, broadcast), as an fp16x8 MFMA operand.  value * scale
+// has at most 6 significant bits and lies in [2^-10, 2688], so both the
+// conversion and the product are exact.  The packed results are consumed
+// whole: this compiler mis-simplifies a scalar extract of the high half of
+// the packed conversion's result.
+__device__ __forceinline__ f16x8 decode8(uint32_t w, _Float16 s) {
+  const f16x2 s2 = {s, s};
+  const f16x2 p0 = e2m1_unpack2_f16<0>(w) * s2;
+  const f16x2 p1 = e2m1_unpack2_f16<1>(w) * s2;
+  const f16x2 p2 = e2m1_unpack2_f16<2>(w) * s2;
+  const f16x2 p3 = e2m1_unpack2_f16<3>(w) * s2;
+  return __builtin_bit_cast(f16x8, u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                         __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

@@ -1,0 +1,393 @@
+// Block-scaled W4A4 NVFP4 GEMM for gfx950.
+//
+// The DiT linear layers run an NVFP4 GEMM on NVFP4 weights and dynamically
+// quantized NVFP4 activations ("NVIDIA介绍用TensorRT LLM VisualGen加速Blackwell
+// 上的FLUX 3 Image Klein", sns.style, time-breakdown paragraph; "NVIDIA
+// показала, как сократить генерацию FLUX 3 Image Klein с 22 до 6 секунд",
+// xalabuda.com, section "Квантование NVFP4 и оптимизация вычислительных ядер"):
+//
+//   Y[m,n] = bf16( epi( sA*sW * sum_k Ahat[m,k]*What[n,k] + bias[n] ) )
+//
+// Exact decode.  value(E2M1) * E4M3 has at most 6 significant bits and lies
+// in [2^-10, 2688]: it is exact in fp16.  Each wave decodes its own operand
+// fragments in registers -- the gfx950 packed E2M1->fp16 conversion (scale 1.0,
+// which it applies as an exponent only) and one packed fp16 multiply by the
+// block scale -- and feeds v_mfma_f32_32x32x16_f16, so the products are exact
+// and only the fp32 accumulation rounds.  The per-tensor scales are applied
+// once in the epilogue.
+//
+// Layout of the work:
+//   * workgroup = 4 waves in 2x2, output tile BM x BN, each wave BM/2 x BN/2
+//     (4x4 MFMA 32x32 tiles at 256x256 -> 256 fp32 accumulators per lane);
+//   * K advances 128 elements (8 blocks) per step; LDS holds the packed codes
+//     (64 B per row and step, rows padded to 80 B) and the block scales already
+//     turned into fp16 pairs (32 B per row, padded to 40 B), double-buffered,
+//     with the next step's global loads held in registers meanwhile;
+//   * K is permuted inside a step, identically for A and W: lanes 0-31 of a
+//     wave take elements 0-63 of the step, lanes 32-63 elements 64-127, so a
+//     lane's codes for the whole step are 32 contiguous bytes of its row (two
+//     128-bit LDS reads) and each lane's 8 elements of one MFMA share a scale.
+//     The MFMA sums over whichever 16 k's it is given; A and W agree on them.
+//   * the tile order is renumbered so each XCD (workgroups are dealt to the 8
+//     XCDs round-robin) walks a contiguous, row-grouped range of tiles and
+//     reuses A and W panels in its own L2.
+#include <cstdlib>
+#include <cstring>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kBK = 128;               // K elements per step
+constexpr int kCodePitch = 80;         // LDS bytes per row of codes (64 used)
+constexpr int kScalePitch = 20;        // LDS bytes per row of fp16 scales (16 used)
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+// Tile shape BM x BN, WGM x WGN waves (each owns a WM x WN sub-tile of 32x32
+// MFMA tiles), MINB workgroups per CU requested from the register allocator.
+template <int BM_, int BN_, int WGM_, int WGN_, int MINB_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, MINB = MINB_;
+  static constexpr int NT = 64 * WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int A_CODES = 0;
+  static constexpr int B_CODES = A_CODES + BM * kCodePitch;
+  static constexpr int A_SC = B_CODES + BN * kCodePitch;
+  static constexpr int B_SC = A_SC + BM * kScalePitch;
+  static constexpr int STAGE = B_SC + BN * kScalePitch;
+  static constexpr int A_CHUNKS = BM * 4 / NT;   // 16-byte code chunks per thread
+  static constexpr int B_CHUNKS = BN * 4 / NT;
+  static_assert(BM * 4 % NT == 0 && BN * 4 % NT == 0, "loader split");
+  static_assert(BM <= NT && BN <= NT, "one scale row per thread");
+  static_assert(TM >= 1 && TN >= 1, "wave tile");
+};
+
+struct Operand {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int64_t rows;
+};
+
+template <class C>
+struct Staged {
+  u32x4 a[C::A_CHUNKS];
+  u32x4 b[C::B_CHUNKS];
+  u32x2 sa, sb;
+};
+
+// 16 bytes of codes = 2 blocks of row `row`, starting at block `kb`.
+__device__ __forceinline__ u32x4 load_code_chunk(const Operand& op, int64_t row, int64_t kb,
+                                                 int64_t kblocks, bool vec16) {
+  if (row >= op.rows || kb >= kblocks) return u32x4{0u, 0u, 0u, 0u};
+  const uint8_t* p = op.codes + row * (kblocks * 8) + kb * 8;
+  if (kb + 2 <= kblocks) {
+    if (vec16) return *reinterpret_cast<const u32x4*>(p);
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
+  }
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+  return u32x4{lo.x, lo.y, 0u, 0u};
+}
+
+// The 8 scale bytes of row `row` for blocks kb .. kb+7 (zero past the end).
+__device__ __forceinline__ u32x2 load_scale8(const Operand& op, int64_t row, int64_t kb,
+                                             int64_t kblocks, bool vec8) {
+  if (row >= op.rows) return u32x2{0u, 0u};
+  const uint8_t* p = op.scales + row * kblocks + kb;
+  if (vec8 && kb + 8 <= kblocks) return *reinterpret_cast<const u32x2*>(p);
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (kb + i < kblocks) w[i >> 2] |= (uint32_t)p[i] << (8 * (i & 3));
+  return u32x2{w[0], w[1]};
+}
+
+// Global -> registers for K step kt.  kEdge: rows or K may run past the end
+// (zero fill, narrow loads); otherwise every access is a full 16 / 8-byte load.
+template <class C, bool kEdge>
+__device__ __forceinline__ void load_stage(const Operand& A, const Operand& W, int64_t m0,
+                                           int64_t n0, int kt, int64_t kblocks, bool vec16,
+                                           bool vec8, Staged<C>& s) {
+  using T = C;
+  constexpr int BM = C::BM, BN = C::BN;
+  const int64_t kb0 = (int64_t)kt * (kBK / 16);
+#pragma unroll
+  for (int i = 0; i < T::A_CHUNKS; ++i) {
+    const int q = threadIdx.x + i * C::NT;
+    if constexpr (kEdge)
+      s.a[i] = load_code_chunk(A, m0 + (q >> 2), kb0 + (q & 3) * 2, kblocks, vec16);
+    else
+      s.a[i] = *reinterpret_cast<const u32x4*>(A.codes + (m0 + (q >> 2)) * (kblocks * 8) +
+                                               (kb0 + (q & 3) * 2) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < T::B_CHUNKS; ++i) {
+    const int q = threadIdx.x + i * C::NT;
+    if constexpr (kEdge)
+      s.b[i] = load_code_chunk(W, n0 + (q >> 2), kb0 + (q & 3) * 2, kblocks, vec16);
+    else
+      s.b[i] = *reinterpret_cast<const u32x4*>(W.codes + (n0 + (q >> 2)) * (kblocks * 8) +
+                                               (kb0 + (q & 3) * 2) * 8);
+  }
+  if constexpr (kEdge) {
+    if (threadIdx.x < BM) s.sa = load_scale8(A, m0 + threadIdx.x, kb0, kblocks, vec8);
+    if (threadIdx.x < BN) s.sb = load_scale8(W, n0 + threadIdx.x, kb0, kblocks, vec8);
+  } else {
+    if (threadIdx.x < BM)
+      s.sa = *reinterpret_cast<const u32x2*>(A.scales + (m0 + threadIdx.x) * kblocks + kb0);
+    if (threadIdx.x < BN)
+      s.sb = *reinterpret_cast<const u32x2*>(W.scales + (n0 + threadIdx.x) * kblocks + kb0);
+  }
+}
+
+// Eight E4M3 scale bytes -> eight fp16 (exact) in LDS, two per dword.
+__device__ __forceinline__ void store_scales(u32x2 sc, uint8_t* dst) {
+  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+  d[0] = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<false>(sc.x));
+  d[1] = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<true>(sc.x));
+  d[2] = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<false>(sc.y));
+  d[3] = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<true>(sc.y));
+}
+
+template <class C>
+__device__ __forceinline__ void store_stage(const Staged<C>& s, uint8_t* stage) {
+  using T = C;
+  constexpr int BM = C::BM, BN = C::BN;
+#pragma unroll
+  for (int i = 0; i < T::A_CHUNKS; ++i) {
+    const int q = threadIdx.x + i * C::NT;
+    *reinterpret_cast<u32x4*>(stage + T::A_CODES + (q >> 2) * kCodePitch + (q & 3) * 16) = s.a[i];
+  }
+#pragma unroll
+  for (int i = 0; i < T::B_CHUNKS; ++i) {
+    const int q = threadIdx.x + i * C::NT;
+    *reinterpret_cast<u32x4*>(stage + T::B_CODES + (q >> 2) * kCodePitch + (q & 3) * 16) = s.b[i];
+  }
+  if (threadIdx.x < BM) store_scales(s.sa, stage + T::A_SC + threadIdx.x * kScalePitch);
+  if (threadIdx.x < BN) store_scales(s.sb, stage + T::B_SC + threadIdx.x * kScalePitch);
+}
+
+template <class C>
+__device__ __forceinline__ void compute_stage(const uint8_t* stage,
+                                              f32x16 (&acc)[C::TM][C::TN]) {
+  using T = C;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    u32x4 ca[T::TM], cb[T::TN];
+    f16x2 sa[T::TM], sb[T::TN];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) {
+      const int row = wm * T::WM + i * 32 + r;
+      ca[i] = *reinterpret_cast<const u32x4*>(stage + T::A_CODES + row * kCodePitch + h * 32 + half * 16);
+      sa[i] = *reinterpret_cast<const f16x2*>(stage + T::A_SC + row * kScalePitch + h * 8 + half * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+      const int row = wn * T::WN + j * 32 + r;
+      cb[j] = *reinterpret_cast<const u32x4*>(stage + T::B_CODES + row * kCodePitch + h * 32 + half * 16);
+      sb[j] = *reinterpret_cast<const f16x2*>(stage + T::B_SC + row * kScalePitch + h * 8 + half * 4);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      f16x8 av[T::TM], bv[T::TN];
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i) {
+        const uint32_t w = kk == 0 ? ca[i].x : kk == 1 ? ca[i].y : kk == 2 ? ca[i].z : ca[i].w;
+        av[i] = decode8(w, kk < 2 ? sa[i].x : sa[i].y);
+      }
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+        const uint32_t w = kk == 0 ? cb[j].x : kk == 1 ? cb[j].y : kk == 2 ? cb[j].z : cb[j].w;
+        bv[j] = decode8(w, kk < 2 ? sb[j].x : sb[j].y);
+      }
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+template <class C, bool kEdge>
+__device__ __forceinline__ void main_loop(const Operand& A, const Operand& Wt, int64_t m0,
+                                          int64_t n0, int64_t K, bool vec16, bool vec8,
+                                          uint8_t* lds,
+                                          f32x16 (&acc)[C::TM][C::TN]) {
+  using T = C;
+  const int64_t kblocks = K / 16;
+  const int nk = (int)((K + kBK - 1) / kBK);
+  Staged<C> st;
+  load_stage<C, kEdge>(A, Wt, m0, n0, 0, kblocks, vec16, vec8, st);
+  store_stage<C>(st, lds);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    uint8_t* cur = lds + (kt & 1) * T::STAGE;
+    uint8_t* nxt = lds + ((kt + 1) & 1) * T::STAGE;
+    // Prefetch the next step unconditionally (the last step re-reads itself
+    // into the idle buffer): a conditional prefetch gets sunk next to its LDS
+    // stores, and every step then waits out the full memory latency.
+    const int kn = kt + 1 < nk ? kt + 1 : kt;
+    load_stage<C, kEdge>(A, Wt, m0, n0, kn, kblocks, vec16, vec8, st);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage<C>(cur, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    store_stage<C>(st, nxt);
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+
+// Tile index of this workgroup: XCD-contiguous ranges, then row-grouped order.
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                            int64_t& tn) {
+  const int64_t T = tiles_m * tiles_n;
+  const int64_t b = blockIdx.x;
+  const int64_t xcd = b % kXcds, slot = b / kXcds;
+  // workgroups with id % 8 == k: n_k = ceil((T - k) / 8); start_k = sum_{j<k} n_j
+  int64_t start = 0;
+  for (int64_t k = 0; k < xcd; ++k) start += (T - k + kXcds - 1) / kXcds;
+  const int64_t t = start + slot;
+  const int64_t per_group = kGroupM * tiles_n;
+  const int64_t group = t / per_group;
+  const int64_t first_m = group * kGroupM;
+  const int64_t gsize = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const int64_t in_group = t - group * per_group;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ sa, const uint8_t* __restrict__ w_codes,
+    const uint8_t* __restrict__ w_scales, const float* __restrict__ sw,
+    const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi,
+    uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax, int vec_flags) {
+  using T = C;
+  constexpr int BM = C::BM, BN = C::BN;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * T::STAGE];
+
+  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const bool vec16 = vec_flags & 1, vec8 = vec_flags & 2;
+  const Operand A{a_codes, a_scales, M}, Wt{w_codes, w_scales, N};
+
+  f32x16 acc[T::TM][T::TN];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) acc[i][j] = f32x16{};
+
+  const bool interior = m0 + BM <= M && n0 + BN <= N && K % kBK == 0 && vec16 && vec8;
+  if (interior)
+    main_loop<C, false>(A, Wt, m0, n0, K, vec16, vec8, lds, acc);
+  else
+    main_loop<C, true>(A, Wt, m0, n0, K, vec16, vec8, lds, acc);
+
+  // epilogue: sA*sW, bias, GELU, bf16 round-to-nearest-even, optional amax
+  const float scale = (*sa) * (*sw);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < T::TN; ++j) {
+    const int64_t col = n0 + wn * T::WN + j * 32 + (lane & 31);
+    const bool col_ok = col < N;
+    const float bv = (bias && col_ok) ? bf16_bits_to_f32(bias[col]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * T::WM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        if (col_ok && row < M) {
+          float v = acc[i][j][e] * scale + bv;
+          if (epi == 1) v = gelu_erf(v);
+          const uint32_t hb = bf16_rne_bits(v);
+          y[row * N + col] = (uint16_t)hb;
+          const uint32_t mag = (hb & 0x7FFFu) << 16;
+          amax = amax > mag ? amax : mag;
+        }
+      }
+  }
+  if (y_amax) {
+    amax = wave_max_u32(amax);
+    if (lane == 0) atomicMax(y_amax, amax);
+  }
+}
+
+__global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
+
+template <class C>
+hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const float* sa,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* sw,
+                       const void* bias, int64_t M, int64_t N, int64_t K, int epi, void* y,
+                       uint32_t* amax, hipStream_t stream) {
+  const int64_t tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  const uintptr_t align_bits = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(w_codes);
+  const bool vec16 = (K % 32 == 0) && (align_bits & 15) == 0;
+  const uintptr_t salign = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(w_scales);
+  const bool vec8 = ((K / 16) % 8 == 0) && (salign & 7) == 0;
+  hipLaunchKernelGGL((gemm_nvfp4_kernel<C>), dim3((unsigned)tiles), dim3(C::NT), 0, stream,
+                     a_codes, a_scales, sa, w_codes, w_scales, sw,
+                     reinterpret_cast<const uint16_t*>(bias), M, N, K, epi,
+                     reinterpret_cast<uint16_t*>(y), amax, (vec16 ? 1 : 0) | (vec8 ? 2 : 0));
+  return hipGetLastError();
+}
+
+using Cfg256x256w4 = Cfg<256, 256, 2, 2, 1>;   // 4 waves of 128x128
+using Cfg256x256w8 = Cfg<256, 256, 2, 4, 1>;   // 8 waves of 128x64
+using Cfg256x256w8t = Cfg<256, 256, 4, 2, 1>;  // 8 waves of 64x128
+using Cfg256x128w4 = Cfg<256, 128, 2, 2, 1>;   // 4 waves of 128x64
+using Cfg256x128w8 = Cfg<256, 128, 4, 2, 1>;   // 8 waves of 64x64
+using Cfg128x128w4 = Cfg<128, 128, 2, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU
+
+}  // namespace
+
+hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales,
+                             const float* a_tensor_scale, const uint8_t* w_codes,
+                             const uint8_t* w_scales, const float* w_tensor_scale,
+                             const void* bias, int64_t M, int64_t N, int64_t K, int epilogue,
+                             void* y, float* y_amax, hipStream_t stream) {
+  uint32_t* amax = reinterpret_cast<uint32_t*>(y_amax);
+  if (amax) {
+    hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, stream, amax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (M == 0 || N == 0) return hipSuccess;
+  // 256x256 tiles with 8 waves (two per SIMD, so one wave's MFMAs overlap the
+  // other's decode and LDS traffic) for DiT-sized problems; 128x128 tiles, two
+  // workgroups per CU, below that.
+  int choice = 5;
+  if (M * N > (int64_t)256 * 256 * 128) choice = 2;
+  const char* force = getenv("NVFP4_GEMM_CFG");   // debug pinning of the tile configuration
+  if (force && force[0] >= '0' && force[0] <= '5') choice = force[0] - '0';
+#define NVFP4_LAUNCH(CFG)                                                                     \
+  return launch_tile<CFG>(a_codes, a_scales, a_tensor_scale, w_codes, w_scales, w_tensor_scale, \
+                          bias, M, N, K, epilogue, y, amax, stream)
+  switch (choice) {
+    case 0: NVFP4_LAUNCH(Cfg256x256w4);
+    case 1: NVFP4_LAUNCH(Cfg256x256w8);
+    case 2: NVFP4_LAUNCH(Cfg256x256w8t);
+    case 3: NVFP4_LAUNCH(Cfg256x128w4);
+    case 4: NVFP4_LAUNCH(Cfg256x128w8);
+    default: NVFP4_LAUNCH(Cfg128x128w4);
+  }
+#undef NVFP4_LAUNCH
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,144 @@
+// Probes of the gfx950 conversions the NVFP4 kernels rely on, exposed through
+// include/nvfp4_isa_probe.h so tests can compare them with the CPU oracle on
+// every input the kernels can give them.  Each probe calls the same device
+// helpers the kernels call (device_common.hpp), never a copy of them.
+//
+//   * E2M1 encode (quantizer): a monotone step function of the binary32 bit
+//     pattern, so scanning every pattern of a range and reporting where the
+//     code changes characterises it completely.  All four byte positions of
+//     the packed conversion are exercised and must agree.
+//   * E4M3 encode (quantizer, integer arithmetic): the same scan.
+//   * E2M1 decode to fp16 / fp32 and E4M3 decode to fp16 / fp32 (GEMM
+//     loader, dequantizer): every byte value in every byte position.
+#include "device_common.hpp"
+#include "nvfp4_isa_probe.h"
+
+namespace {
+
+using namespace nvfp4;
+
+template <int MODE>
+__device__ __forceinline__ uint32_t probe_code(uint32_t bits) {
+  const float v = __uint_as_float(bits);
+  if constexpr (MODE == 0) {
+    // pack the same value into both nibbles of each byte position
+    uint32_t w = 0;
+    w = e2m1_pack2<0>(w, v, v);
+    w = e2m1_pack2<1>(w, v, v);
+    w = e2m1_pack2<2>(w, v, v);
+    w = e2m1_pack2<3>(w, v, v);
+    return w;   // 8 nibbles that must all be equal
+  } else {
+    return e4m3_from_f32_rne(v);
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void transitions_kernel(uint32_t lo, uint32_t nchunks,
+                                                          uint32_t* list, uint32_t cap,
+                                                          uint32_t* count, uint32_t* mismatch) {
+  const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nchunks) return;
+  const uint32_t base = lo + (uint32_t)(t * 256u);
+  uint32_t prev = 0;
+  for (uint32_t i = 0; i <= 256; ++i) {
+    const uint32_t p = base + i;
+    uint32_t c = probe_code<MODE>(p);
+    if constexpr (MODE == 0) {
+      if (c != (c & 0xFu) * 0x11111111u) atomicAdd(mismatch, 1u);
+      c &= 0xFu;
+    }
+    if (i > 0 && c != prev) {
+      const uint32_t slot = atomicAdd(count, 1u);
+      if (slot < cap) {
+        list[3 * slot] = p;
+        list[3 * slot + 1] = prev;
+        list[3 * slot + 2] = c;
+      }
+    }
+    prev = c;
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void encode_kernel(const uint32_t* bits, int n, uint32_t* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = probe_code<MODE>(bits[i]);
+}
+
+// For item i (word w = words[i], E4M3 byte b = sbytes[i] & 0xFF):
+//   e2m1_f16 [i][8]: the GEMM operand decode8(w, fp16(b)), element 0 first;
+//   e2m1_f32 [i][8]: the dequantizer's E2M1 -> fp32 conversion of w;
+//   e4m3_f16 [i][4]: the four bytes of w as E4M3 through the hardware pair
+//                    conversion the GEMM loader uses;
+//   e4m3_f32 [i][4]: the four bytes of w through the integer E4M3 decoder.
+// Outputs are written as whole packed words.
+__global__ __launch_bounds__(256) void decode_kernel(const uint32_t* words, const uint32_t* sbytes,
+                                                     int n, uint32_t* e2m1_f16, float* e2m1_f32,
+                                                     uint32_t* e4m3_f16, float* e4m3_f32) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t w = words[i];
+  const uint32_t sp = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<false>(sbytes[i] & 0xFFu));
+  const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(sp & 0xFFFFu));
+  const u32x4 d = __builtin_bit_cast(u32x4, decode8(w, s));
+  reinterpret_cast<u32x4*>(e2m1_f16)[i] = d;
+  const f32x2 f[4] = {e2m1_unpack2_f32<0>(w), e2m1_unpack2_f32<1>(w), e2m1_unpack2_f32<2>(w),
+                      e2m1_unpack2_f32<3>(w)};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    e2m1_f32[8 * i + 2 * j] = f[j].x;
+    e2m1_f32[8 * i + 2 * j + 1] = f[j].y;
+  }
+  e4m3_f16[2 * i] = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<false>(w));
+  e4m3_f16[2 * i + 1] = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<true>(w));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) e4m3_f32[4 * i + j] = e4m3_to_f32((w >> (8 * j)) & 0xFFu);
+}
+
+bool bad_ptr(const void* p) { return p == nullptr; }
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_probe_transitions(int which, uint32_t lo, uint32_t nchunks, uint32_t* list, uint32_t cap,
+                            uint32_t* count, uint32_t* mismatch, void* stream) {
+  if (bad_ptr(list) || bad_ptr(count) || bad_ptr(mismatch)) return -1;
+  if (which < 0 || which > 1 || nchunks == 0 || (uint64_t)lo + (uint64_t)nchunks * 256u > 0xFFFFFFFFull)
+    return -2;
+  const dim3 grid((nchunks + 255) / 256), block(256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (which == 0)
+    hipLaunchKernelGGL(transitions_kernel<0>, grid, block, 0, s, lo, nchunks, list, cap, count, mismatch);
+  else
+    hipLaunchKernelGGL(transitions_kernel<1>, grid, block, 0, s, lo, nchunks, list, cap, count, mismatch);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int nvfp4_probe_encode(int which, const uint32_t* bits, int n, uint32_t* out, void* stream) {
+  if (bad_ptr(bits) || bad_ptr(out)) return -1;
+  if (which < 0 || which > 1 || n <= 0) return -2;
+  const dim3 grid((n + 255) / 256), block(256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (which == 0)
+    hipLaunchKernelGGL(encode_kernel<0>, grid, block, 0, s, bits, n, out);
+  else
+    hipLaunchKernelGGL(encode_kernel<1>, grid, block, 0, s, bits, n, out);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int nvfp4_probe_decode(const uint32_t* words, const uint32_t* sbytes, int n, uint16_t* e2m1_f16,
+                       float* e2m1_f32, uint16_t* e4m3_f16, float* e4m3_f32, void* stream) {
+  if (bad_ptr(words) || bad_ptr(sbytes) || bad_ptr(e2m1_f16) || bad_ptr(e2m1_f32) ||
+      bad_ptr(e4m3_f16) || bad_ptr(e4m3_f32))
+    return -1;
+  if (n <= 0) return -2;
+  hipLaunchKernelGGL(decode_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), words, sbytes, n,
+                     reinterpret_cast<uint32_t*>(e2m1_f16), e2m1_f32,
+                     reinterpret_cast<uint32_t*>(e4m3_f16), e4m3_f32);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+}  // extern "C"
