@@ -43,6 +43,11 @@ int nvfp4_probe_encode(int which, const uint32_t* bits, int n, uint32_t* out, vo
 int nvfp4_probe_decode(const uint32_t* words, const uint32_t* sbytes, int n, uint16_t* e2m1_f16,
                        float* e2m1_f32, uint16_t* e4m3_f16, float* e4m3_f32, void* stream);
 
+/* For n (even) binary32 inputs: bf16[i] = their bf16 rounding through the GEMM
+ * epilogue's packed conversion (4-byte aligned output); gelu[i] = the
+ * epilogue's erf-form GELU. */
+int nvfp4_probe_bf16_gelu(const float* in, int n, uint16_t* bf16, float* gelu, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,36 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two binary32 -> two bf16 (low half = lo), round-to-nearest-even, through the
+// gfx950 packed conversion.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// erf-form GELU, z * Phi(z) with Phi(z) = erfc(-z / sqrt 2) / 2.  erfc is the
+// Chebyshev fit "erfcc" of Numerical Recipes (section 6.2, fractional error
+// below 1.2e-7 for every argument), so the result is accurate relative to
+// |GELU(z)| in both tails; the remaining error is a few binary32 ulps from
+// the approximate reciprocal and exponential.
+__device__ __forceinline__ float gelu_erf(float z) {
+  const float x = __builtin_fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, x, 1.0f));
+  float q = 0.17087277f;
+  q = __builtin_fmaf(q, t, -0.82215223f);
+  q = __builtin_fmaf(q, t, 1.48851587f);
+  q = __builtin_fmaf(q, t, -1.13520398f);
+  q = __builtin_fmaf(q, t, 0.27886807f);
+  q = __builtin_fmaf(q, t, -0.18628806f);
+  q = __builtin_fmaf(q, t, 0.09678418f);
+  q = __builtin_fmaf(q, t, 0.37409196f);
+  q = __builtin_fmaf(q, t, 1.00002368f);
+  const float arg = __builtin_fmaf(t, q, __builtin_fmaf(-x, x, -1.26551223f));
+  const float y = t * __builtin_amdgcn_exp2f(arg * 1.44269504088896341f);   // erfc(x)
+  return z * (z >= 0.0f ? __builtin_fmaf(-0.5f, y, 1.0f) : 0.5f * y);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }

@@ -83,10 +83,6 @@ __device__ __forceinline__ void mma_step(const uint16_t* __restrict__ As,
 
 // ----------------------------------------------------------------- epilogue --
 
-__device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
-}
-
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[2][2], float scale,
                                          const uint16_t* __restrict__ bias, int epi, int64_t M,
                                          int64_t N, int64_t m0, int64_t n0,

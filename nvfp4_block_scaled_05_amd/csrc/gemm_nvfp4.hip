@@ -245,8 +245,63 @@ __device__ __forceinline__ void main_loop(const Operand& A, const Operand& Wt, i
   }
 }
 
-__device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+// Epilogue: acc * sA*sW + bias (one fused multiply-add), optional GELU, bf16
+// round-to-nearest-even, optional max |bf16 y| (one atomic per wave).  The
+// amax is tracked on the binary32 values and rounded once at the end: bf16
+// rounding is monotone, so this equals the max of the rounded outputs.
+// A lane holds, per 32x32 tile, column (lane % 32) of rows
+// (e/4)*8 + (lane/32)*4 + e%4; rows e, e+1 are packed by one conversion.
+template <class C>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::TM][C::TN], float scale,
+                                         const uint16_t* __restrict__ bias, int epi, int64_t M,
+                                         int64_t N, int64_t m0, int64_t n0,
+                                         uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int64_t r0 = m0 + wm * C::WM + (lane >> 5) * 4;
+  const int64_t c0 = n0 + wn * C::WN + (lane & 31);
+  const bool full = m0 + C::BM <= M && n0 + C::BN <= N && (int64_t)C::BM * N < ((int64_t)1 << 30);
+  uint16_t* __restrict__ yt = y + r0 * N + c0;   // this lane's first element
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) {
+    const int64_t col = c0 + j * 32;
+    const bool col_ok = col < N;
+    const float bv = (bias && col_ok) ? bf16_bits_to_f32(bias[col]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const int dr = i * 32 + (e >> 2) * 8 + (e & 3);       // row offset from r0
+        float v0 = __builtin_fmaf(acc[i][j][e], scale, bv);
+        float v1 = __builtin_fmaf(acc[i][j][e + 1], scale, bv);
+        if (epi == 1) {
+          v0 = gelu_erf(v0);
+          v1 = gelu_erf(v1);
+        }
+        const uint32_t pk = bf16x2_rne(v0, v1);
+        if (full) {
+          const uint32_t off = (uint32_t)dr * (uint32_t)N + (uint32_t)(j * 32);
+          yt[off] = (uint16_t)pk;
+          yt[off + (uint32_t)N] = (uint16_t)(pk >> 16);
+          amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)));
+        } else if (col_ok) {
+          if (r0 + dr < M) {
+            y[(r0 + dr) * N + col] = (uint16_t)pk;
+            amax = __builtin_fmaxf(amax, __builtin_fabsf(v0));
+          }
+          if (r0 + dr + 1 < M) {
+            y[(r0 + dr + 1) * N + col] = (uint16_t)(pk >> 16);
+            amax = __builtin_fmaxf(amax, __builtin_fabsf(v1));
+          }
+        }
+      }
+  }
+  if (y_amax) {
+    uint32_t a = (bf16x2_rne(amax, 0.0f) & 0xFFFFu) << 16;
+    a = wave_max_u32(a);
+    if (lane == 0) atomicMax(y_amax, a);
+  }
 }
 
 // Tile index of this workgroup: XCD-contiguous ranges, then row-grouped order.
@@ -298,35 +353,317 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_kernel(
   else
     main_loop<C, true>(A, Wt, m0, n0, K, vec16, vec8, lds, acc);
 
-  // epilogue: sA*sW, bias, GELU, bf16 round-to-nearest-even, optional amax
-  const float scale = (*sa) * (*sw);
+  epilogue<C>(acc, (*sa) * (*sw), bias, epi, M, N, m0, n0, y, y_amax);
+}
+
+// ---------------------------------------------------------------------------
+// v2: the weight operand is decoded once per workgroup into LDS as fp16 and
+// shared by every wave-row; the activation operand stays packed in LDS and is
+// decoded by each wave in registers.  K advances 64 elements per step.  Same
+// K permutation as above at half width: lanes 0-31 take elements 0-31 of the
+// step, lanes 32-63 elements 32-63.
+// ---------------------------------------------------------------------------
+constexpr int kBK2 = 64;
+constexpr int kACodePitch2 = 48;      // 32 B of codes per row and step
+constexpr int kAScalePitch2 = 12;     // 4 fp16 block scales per row and step
+constexpr int kWPitch2 = 144;         // 64 fp16 of decoded weight per row and step
+
+template <class C>
+struct Lay2 {
+  static constexpr int A_CODES = 0;
+  static constexpr int A_SC = A_CODES + C::BM * kACodePitch2;
+  static constexpr int W_F16 = A_SC + C::BM * kAScalePitch2;
+  static constexpr int STAGE = W_F16 + C::BN * kWPitch2;
+  static_assert(C::BM * 2 == C::NT && C::BN * 2 == C::NT, "one 16-byte chunk of A and W per thread");
+};
+
+struct Staged2 {
+  u32x4 a;        // 16 B of A codes: 2 blocks
+  u32x4 w;        // 16 B of W codes: 2 blocks
+  uint32_t sa;    // 4 A scale bytes (threads < BM)
+  uint32_t sw;    // 2 W scale bytes for this thread's chunk
+};
+
+template <class C, bool kEdge>
+__device__ __forceinline__ void load_stage2(const Operand& A, const Operand& W, int64_t m0,
+                                            int64_t n0, int kt, int64_t kblocks, Staged2& s) {
+  const int q = threadIdx.x;
+  const int64_t kb0 = (int64_t)kt * (kBK2 / 16);
+  const int64_t ra = m0 + (q >> 1), rw = n0 + (q >> 1);
+  const int64_t kb = kb0 + (q & 1) * 2;
+  if constexpr (kEdge) {
+    s.a = load_code_chunk(A, ra, kb, kblocks, false);
+    s.w = load_code_chunk(W, rw, kb, kblocks, false);
+    uint32_t sa = 0, sw = 0;
+    if (q < C::BM && m0 + q < A.rows) {
+      const uint8_t* p = A.scales + (m0 + q) * kblocks;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (kb0 + i < kblocks) sa |= (uint32_t)p[kb0 + i] << (8 * i);
+    }
+    if (rw < W.rows) {
+      const uint8_t* p = W.scales + rw * kblocks;
+      if (kb < kblocks) sw |= p[kb];
+      if (kb + 1 < kblocks) sw |= (uint32_t)p[kb + 1] << 8;
+    }
+    s.sa = sa;
+    s.sw = sw;
+  } else {
+    s.a = *reinterpret_cast<const u32x4*>(A.codes + ra * (kblocks * 8) + kb * 8);
+    s.w = *reinterpret_cast<const u32x4*>(W.codes + rw * (kblocks * 8) + kb * 8);
+    if (q < C::BM) s.sa = *reinterpret_cast<const uint32_t*>(A.scales + (m0 + q) * kblocks + kb0);
+    s.sw = *reinterpret_cast<const uint16_t*>(W.scales + rw * kblocks + kb);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void store_stage2(const Staged2& s, uint8_t* stage) {
+  using L = Lay2<C>;
+  const int q = threadIdx.x;
+  const int row = q >> 1, c = q & 1;
+  *reinterpret_cast<u32x4*>(stage + L::A_CODES + row * kACodePitch2 + c * 16) = s.a;
+  if (q < C::BM) {
+    uint32_t* d = reinterpret_cast<uint32_t*>(stage + L::A_SC + q * kAScalePitch2);
+    d[0] = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<false>(s.sa));
+    d[1] = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<true>(s.sa));
+  }
+  // decode this thread's 32 weight elements (2 blocks) to fp16
+  const uint32_t sp = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<false>(s.sw));
+  const _Float16 s0 = __builtin_bit_cast(_Float16, (uint16_t)(sp & 0xFFFFu));
+  const _Float16 s1 = __builtin_bit_cast(_Float16, (uint16_t)(sp >> 16));
+  u32x4* d = reinterpret_cast<u32x4*>(stage + L::W_F16 + row * kWPitch2 + c * 64);
+  d[0] = __builtin_bit_cast(u32x4, decode8(s.w.x, s0));
+  d[1] = __builtin_bit_cast(u32x4, decode8(s.w.y, s0));
+  d[2] = __builtin_bit_cast(u32x4, decode8(s.w.z, s1));
+  d[3] = __builtin_bit_cast(u32x4, decode8(s.w.w, s1));
+}
+
+template <class C>
+__device__ __forceinline__ void compute_stage2(const uint8_t* stage, f32x16 (&acc)[C::TM][C::TN]) {
+  using L = Lay2<C>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
-  uint32_t amax = 0;
+  const int r = lane & 31, h = lane >> 5;
+  u32x4 ca[C::TM];
+  f16x2 sa[C::TM];
 #pragma unroll
-  for (int j = 0; j < T::TN; ++j) {
-    const int64_t col = n0 + wn * T::WN + j * 32 + (lane & 31);
-    const bool col_ok = col < N;
-    const float bv = (bias && col_ok) ? bf16_bits_to_f32(bias[col]) : 0.0f;
+  for (int i = 0; i < C::TM; ++i) {
+    const int row = wm * C::WM + i * 32 + r;
+    ca[i] = *reinterpret_cast<const u32x4*>(stage + L::A_CODES + row * kACodePitch2 + h * 16);
+    sa[i] = *reinterpret_cast<const f16x2*>(stage + L::A_SC + row * kAScalePitch2 + h * 4);
+  }
 #pragma unroll
-    for (int i = 0; i < T::TM; ++i)
+  for (int kk = 0; kk < 4; ++kk) {
+    f16x8 av[C::TM], bv[C::TN];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * T::WM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        if (col_ok && row < M) {
-          float v = acc[i][j][e] * scale + bv;
-          if (epi == 1) v = gelu_erf(v);
-          const uint32_t hb = bf16_rne_bits(v);
-          y[row * N + col] = (uint16_t)hb;
-          const uint32_t mag = (hb & 0x7FFFu) << 16;
-          amax = amax > mag ? amax : mag;
-        }
+    for (int j = 0; j < C::TN; ++j) {
+      const int row = wn * C::WN + j * 32 + r;
+      bv[j] = *reinterpret_cast<const f16x8*>(stage + L::W_F16 + row * kWPitch2 + (h * 32 + kk * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      const uint32_t w = kk == 0 ? ca[i].x : kk == 1 ? ca[i].y : kk == 2 ? ca[i].z : ca[i].w;
+      av[i] = decode8(w, kk < 2 ? sa[i].x : sa[i].y);
+    }
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+template <class C, bool kEdge>
+__device__ __forceinline__ void main_loop2(const Operand& A, const Operand& Wt, int64_t m0,
+                                           int64_t n0, int64_t K, uint8_t* lds,
+                                           f32x16 (&acc)[C::TM][C::TN]) {
+  using L = Lay2<C>;
+  const int64_t kblocks = K / 16;
+  const int nk = (int)((K + kBK2 - 1) / kBK2);
+  Staged2 st;
+  load_stage2<C, kEdge>(A, Wt, m0, n0, 0, kblocks, st);
+  store_stage2<C>(st, lds);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    uint8_t* cur = lds + (kt & 1) * L::STAGE;
+    uint8_t* nxt = lds + ((kt + 1) & 1) * L::STAGE;
+    const int kn = kt + 1 < nk ? kt + 1 : kt;     // unconditional prefetch (see main_loop)
+    load_stage2<C, kEdge>(A, Wt, m0, n0, kn, kblocks, st);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage2<C>(cur, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    store_stage2<C>(st, nxt);
+    __syncthreads();
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_wlds_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ sa, const uint8_t* __restrict__ w_codes,
+    const uint8_t* __restrict__ w_scales, const float* __restrict__ sw,
+    const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi,
+    uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax, int vec_flags) {
+  using L = Lay2<C>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::STAGE];
+  const int64_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
+  const Operand A{a_codes, a_scales, M}, Wt{w_codes, w_scales, N};
+  f32x16 acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
+  const bool interior = m0 + C::BM <= M && n0 + C::BN <= N && K % kBK2 == 0 && (vec_flags & 4);
+  if (interior)
+    main_loop2<C, false>(A, Wt, m0, n0, K, lds, acc);
+  else
+    main_loop2<C, true>(A, Wt, m0, n0, K, lds, acc);
+  epilogue<C>(acc, (*sa) * (*sw), bias, epi, M, N, m0, n0, y, y_amax);
+}
+
+// v3: v2 with the work of one K step software-pipelined inside each wave --
+// the LDS reads and activation decode of MFMA step kk+1, and (in the second
+// half of the step) the next stage's stores and weight decode, are issued
+// between the MFMAs of step kk, so the matrix pipe runs while the vector ALU
+// decodes (one wave keeps both busy).
+template <class C>
+__device__ __forceinline__ void store_a_stage2(const Staged2& s, uint8_t* stage) {
+  using L = Lay2<C>;
+  const int q = threadIdx.x;
+  *reinterpret_cast<u32x4*>(stage + L::A_CODES + (q >> 1) * kACodePitch2 + (q & 1) * 16) = s.a;
+  if (q < C::BM) {
+    uint32_t* d = reinterpret_cast<uint32_t*>(stage + L::A_SC + q * kAScalePitch2);
+    d[0] = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<false>(s.sa));
+    d[1] = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<true>(s.sa));
+  }
+}
+
+// Quarter `part` (0..3) of this thread's weight decode: 8 elements.
+template <class C>
+__device__ __forceinline__ void store_w_part2(const Staged2& s, uint8_t* stage, int part) {
+  using L = Lay2<C>;
+  const int q = threadIdx.x;
+  const uint32_t sp = __builtin_bit_cast(uint32_t, e4m3_pair_to_f16x2<false>(s.sw));
+  const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(part < 2 ? (sp & 0xFFFFu) : (sp >> 16)));
+  const uint32_t w = part == 0 ? s.w.x : part == 1 ? s.w.y : part == 2 ? s.w.z : s.w.w;
+  u32x4* d = reinterpret_cast<u32x4*>(stage + L::W_F16 + (q >> 1) * kWPitch2 + (q & 1) * 64);
+  d[part] = __builtin_bit_cast(u32x4, decode8(w, sc));
+}
+
+template <class C>
+__device__ __forceinline__ void compute_stage3(const uint8_t* stage, const Staged2& st,
+                                               uint8_t* nxt, f32x16 (&acc)[C::TM][C::TN]) {
+  using L = Lay2<C>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int r = lane & 31, h = lane >> 5;
+  u32x4 ca[C::TM];
+  f16x2 sa[C::TM];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int row = wm * C::WM + i * 32 + r;
+    ca[i] = *reinterpret_cast<const u32x4*>(stage + L::A_CODES + row * kACodePitch2 + h * 16);
+    sa[i] = *reinterpret_cast<const f16x2*>(stage + L::A_SC + row * kAScalePitch2 + h * 4);
+  }
+  f16x8 av[2][C::TM], bv[2][C::TN];
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) {
+    const int row = wn * C::WN + j * 32 + r;
+    bv[0][j] = *reinterpret_cast<const f16x8*>(stage + L::W_F16 + row * kWPitch2 + h * 64);
+  }
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) av[0][i] = decode8(ca[i].x, sa[i].x);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int cur = kk & 1, nx = cur ^ 1;
+    if (kk < 3) {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int row = wn * C::WN + j * 32 + r;
+        bv[nx][j] = *reinterpret_cast<const f16x8*>(stage + L::W_F16 + row * kWPitch2 + h * 64 + (kk + 1) * 16);
       }
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        const uint32_t w = kk == 0 ? ca[i].y : kk == 1 ? ca[i].z : ca[i].w;
+        av[nx][i] = decode8(w, kk + 1 < 2 ? sa[i].x : sa[i].y);
+      }
+    }
+    // the next stage's data is stored in the second half of the step, giving
+    // its global loads (issued at the top of the step) time to arrive
+    if (kk == 2) {
+      store_a_stage2<C>(st, nxt);
+      store_w_part2<C>(st, nxt, 0);
+      store_w_part2<C>(st, nxt, 1);
+    } else if (kk == 3) {
+      store_w_part2<C>(st, nxt, 2);
+      store_w_part2<C>(st, nxt, 3);
+    }
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
+    // interleave: each MFMA followed by a few vector ops and LDS accesses
+#pragma unroll
+    for (int m = 0; m < C::TM * C::TN; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+    }
   }
-  if (y_amax) {
-    amax = wave_max_u32(amax);
-    if (lane == 0) atomicMax(y_amax, amax);
+}
+
+template <class C, bool kEdge>
+__device__ __forceinline__ void main_loop3(const Operand& A, const Operand& Wt, int64_t m0,
+                                           int64_t n0, int64_t K, uint8_t* lds,
+                                           f32x16 (&acc)[C::TM][C::TN]) {
+  using L = Lay2<C>;
+  const int64_t kblocks = K / 16;
+  const int nk = (int)((K + kBK2 - 1) / kBK2);
+  Staged2 st;
+  load_stage2<C, kEdge>(A, Wt, m0, n0, 0, kblocks, st);
+  store_stage2<C>(st, lds);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    uint8_t* cur = lds + (kt & 1) * L::STAGE;
+    uint8_t* nxt = lds + ((kt + 1) & 1) * L::STAGE;
+    const int kn = kt + 1 < nk ? kt + 1 : kt;
+    load_stage2<C, kEdge>(A, Wt, m0, n0, kn, kblocks, st);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage3<C>(cur, st, nxt, acc);
+    __syncthreads();
   }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_pipe_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ sa, const uint8_t* __restrict__ w_codes,
+    const uint8_t* __restrict__ w_scales, const float* __restrict__ sw,
+    const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi,
+    uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax, int vec_flags) {
+  using L = Lay2<C>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::STAGE];
+  const int64_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
+  const Operand A{a_codes, a_scales, M}, Wt{w_codes, w_scales, N};
+  f32x16 acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
+  const bool interior = m0 + C::BM <= M && n0 + C::BN <= N && K % kBK2 == 0 && (vec_flags & 4);
+  if (interior)
+    main_loop3<C, false>(A, Wt, m0, n0, K, lds, acc);
+  else
+    main_loop3<C, true>(A, Wt, m0, n0, K, lds, acc);
+  epilogue<C>(acc, (*sa) * (*sw), bias, epi, M, N, m0, n0, y, y_amax);
 }
 
 __global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
@@ -345,6 +682,29 @@ hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                      a_codes, a_scales, sa, w_codes, w_scales, sw,
                      reinterpret_cast<const uint16_t*>(bias), M, N, K, epi,
                      reinterpret_cast<uint16_t*>(y), amax, (vec16 ? 1 : 0) | (vec8 ? 2 : 0));
+  return hipGetLastError();
+}
+
+template <class C, bool kPipe>
+hipError_t launch_tile2(const uint8_t* a_codes, const uint8_t* a_scales, const float* sa,
+                        const uint8_t* w_codes, const uint8_t* w_scales, const float* sw,
+                        const void* bias, int64_t M, int64_t N, int64_t K, int epi, void* y,
+                        uint32_t* amax, hipStream_t stream) {
+  const int64_t tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  const uintptr_t cal = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(w_codes);
+  const uintptr_t sal = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(w_scales);
+  // interior fast path: 16-byte code rows, 4-byte scale rows
+  const bool vec = (K % 64 == 0) && (cal & 15) == 0 && (sal & 3) == 0;
+  if constexpr (kPipe)
+    hipLaunchKernelGGL((gemm_nvfp4_pipe_kernel<C>), dim3((unsigned)tiles), dim3(C::NT), 0, stream,
+                       a_codes, a_scales, sa, w_codes, w_scales, sw,
+                       reinterpret_cast<const uint16_t*>(bias), M, N, K, epi,
+                       reinterpret_cast<uint16_t*>(y), amax, vec ? 4 : 0);
+  else
+    hipLaunchKernelGGL((gemm_nvfp4_wlds_kernel<C>), dim3((unsigned)tiles), dim3(C::NT), 0, stream,
+                       a_codes, a_scales, sa, w_codes, w_scales, sw,
+                       reinterpret_cast<const uint16_t*>(bias), M, N, K, epi,
+                       reinterpret_cast<uint16_t*>(y), amax, vec ? 4 : 0);
   return hipGetLastError();
 }
 
@@ -369,13 +729,13 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales,
     if (e != hipSuccess) return e;
   }
   if (M == 0 || N == 0) return hipSuccess;
-  // 256x256 tiles with 8 waves (two per SIMD, so one wave's MFMAs overlap the
-  // other's decode and LDS traffic) for DiT-sized problems; 128x128 tiles, two
-  // workgroups per CU, below that.
+  // DiT-sized problems: 256x256 tiles, 8 waves (two per SIMD), the weight
+  // decoded once per workgroup into LDS and the per-wave work software-
+  // pipelined (v3).  Small problems: 128x128 tiles, two workgroups per CU.
   int choice = 5;
-  if (M * N > (int64_t)256 * 256 * 128) choice = 2;
+  if (M * N > (int64_t)256 * 256 * 128) choice = 7;
   const char* force = getenv("NVFP4_GEMM_CFG");   // debug pinning of the tile configuration
-  if (force && force[0] >= '0' && force[0] <= '5') choice = force[0] - '0';
+  if (force && force[0] >= '0' && force[0] <= '7') choice = force[0] - '0';
 #define NVFP4_LAUNCH(CFG)                                                                     \
   return launch_tile<CFG>(a_codes, a_scales, a_tensor_scale, w_codes, w_scales, w_tensor_scale, \
                           bias, M, N, K, epilogue, y, amax, stream)
@@ -385,6 +745,12 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales,
     case 2: NVFP4_LAUNCH(Cfg256x256w8t);
     case 3: NVFP4_LAUNCH(Cfg256x128w4);
     case 4: NVFP4_LAUNCH(Cfg256x128w8);
+    case 6:
+      return launch_tile2<Cfg256x256w8t, false>(a_codes, a_scales, a_tensor_scale, w_codes, w_scales,
+                                                w_tensor_scale, bias, M, N, K, epilogue, y, amax, stream);
+    case 7:
+      return launch_tile2<Cfg256x256w8t, true>(a_codes, a_scales, a_tensor_scale, w_codes, w_scales,
+                                               w_tensor_scale, bias, M, N, K, epilogue, y, amax, stream);
     default: NVFP4_LAUNCH(Cfg128x128w4);
   }
 #undef NVFP4_LAUNCH

@@ -96,6 +96,16 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint32_t* words, cons
   for (int j = 0; j < 4; ++j) e4m3_f32[4 * i + j] = e4m3_to_f32((w >> (8 * j)) & 0xFFu);
 }
 
+// bf16[i] = bf16 rounding of in[i] through the epilogue's packed conversion
+// (pairs i, i+1 converted together); gelu[i] = the epilogue's GELU of in[i].
+__global__ __launch_bounds__(256) void bf16_gelu_kernel(const float* in, int n, uint32_t* bf16,
+                                                        float* gelu) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (2 * i + 1 < n) bf16[i] = bf16x2_rne(in[2 * i], in[2 * i + 1]);
+  if (i < n) gelu[i] = gelu_erf(in[i]);
+  if (i + (n + 1) / 2 < n) gelu[i + (n + 1) / 2] = gelu_erf(in[i + (n + 1) / 2]);
+}
+
 bool bad_ptr(const void* p) { return p == nullptr; }
 
 }  // namespace
@@ -138,6 +148,15 @@ int nvfp4_probe_decode(const uint32_t* words, const uint32_t* sbytes, int n, uin
                      static_cast<hipStream_t>(stream), words, sbytes, n,
                      reinterpret_cast<uint32_t*>(e2m1_f16), e2m1_f32,
                      reinterpret_cast<uint32_t*>(e4m3_f16), e4m3_f32);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int nvfp4_probe_bf16_gelu(const float* in, int n, uint16_t* bf16, float* gelu, void* stream) {
+  if (bad_ptr(in) || bad_ptr(bf16) || bad_ptr(gelu)) return -1;
+  if (n <= 0 || (n & 1)) return -2;
+  const int threads = (n + 1) / 2;
+  hipLaunchKernelGGL(bf16_gelu_kernel, dim3((threads + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), in, n, reinterpret_cast<uint32_t*>(bf16), gelu);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -21,6 +21,9 @@
 // The arithmetic is binary32 round-to-nearest-even throughout: divisions are
 // correctly rounded (no fast-math) and the file is built with FP contraction
 // off, so every value equals the CPU oracle's bit for bit.
+#include <cstdio>
+#include <cstdlib>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -28,30 +31,28 @@ namespace nvfp4 {
 
 static constexpr int kQuantThreads = 256;
 
+__device__ __forceinline__ u16x2 max8(u32x4 a) {
+  return max_u16x2(max_u16x2(abs_halves(a.x), abs_halves(a.y)),
+                   max_u16x2(abs_halves(a.z), abs_halves(a.w)));
+}
+
+// Partial amax: workgroup b scans its contiguous chunk of 16-byte words, U
+// loads in flight per thread, and writes max |x| of the chunk.
+template <int U>
 __global__ __launch_bounds__(kQuantThreads) void amax_partial_kernel(
-    const uint4* __restrict__ x, int64_t n16, uint32_t* __restrict__ partial) {
+    const u32x4* __restrict__ x, int64_t n16, int64_t chunk, uint32_t* __restrict__ partial) {
   u16x2 m = {0, 0};
-  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-  int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    uint4 a = *(x + i);
-    uint4 b = *(x + i + stride);
-    uint4 c = *(x + i + 2 * stride);
-    uint4 d = *(x + i + 3 * stride);
-    m = max_u16x2(m, max_u16x2(max_u16x2(abs_halves(a.x), abs_halves(a.y)),
-                               max_u16x2(abs_halves(a.z), abs_halves(a.w))));
-    m = max_u16x2(m, max_u16x2(max_u16x2(abs_halves(b.x), abs_halves(b.y)),
-                               max_u16x2(abs_halves(b.z), abs_halves(b.w))));
-    m = max_u16x2(m, max_u16x2(max_u16x2(abs_halves(c.x), abs_halves(c.y)),
-                               max_u16x2(abs_halves(c.z), abs_halves(c.w))));
-    m = max_u16x2(m, max_u16x2(max_u16x2(abs_halves(d.x), abs_halves(d.y)),
-                               max_u16x2(abs_halves(d.z), abs_halves(d.w))));
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = lo + chunk < n16 ? lo + chunk : n16;
+  int64_t i = lo + threadIdx.x;
+  for (; i + (U - 1) * kQuantThreads < hi; i += U * kQuantThreads) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = x[i + u * kQuantThreads];
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = max_u16x2(m, max8(v[u]));
   }
-  for (; i < n16; i += stride) {
-    uint4 a = *(x + i);
-    m = max_u16x2(m, max_u16x2(max_u16x2(abs_halves(a.x), abs_halves(a.y)),
-                               max_u16x2(abs_halves(a.z), abs_halves(a.w))));
-  }
+  for (; i < hi; i += kQuantThreads) m = max_u16x2(m, max8(x[i]));
   uint32_t v = m.x > m.y ? m.x : m.y;
   v = wave_max_u32(v);
   __shared__ uint32_t red[kQuantThreads / 64];
@@ -82,8 +83,8 @@ __device__ __forceinline__ uint32_t fold_amax_words(const uint32_t* __restrict__
   return r;
 }
 
-// E2M1 codes of 8 bf16 values (two words of a uint4 half) times e, packed.
-__device__ __forceinline__ uint32_t encode8(uint4 v, float e) {
+// E2M1 codes of 8 bf16 values (one 16-byte word) times e, packed.
+__device__ __forceinline__ uint32_t encode8(u32x4 v, float e) {
   uint32_t c = 0;
   c = e2m1_pack2<0>(c, bf16_bits_to_f32(v.x & 0xFFFFu) * e, bf16_bits_to_f32(v.x >> 16) * e);
   c = e2m1_pack2<1>(c, bf16_bits_to_f32(v.y & 0xFFFFu) * e, bf16_bits_to_f32(v.y >> 16) * e);
@@ -93,7 +94,7 @@ __device__ __forceinline__ uint32_t encode8(uint4 v, float e) {
 }
 
 // Sign-only codes (block scale 0): nibble = 8 for a negative input, else 0.
-__device__ __forceinline__ uint32_t signs8(uint4 v) {
+__device__ __forceinline__ uint32_t signs8(u32x4 v) {
   uint32_t c = 0;
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -104,9 +105,26 @@ __device__ __forceinline__ uint32_t signs8(uint4 v) {
   return c;
 }
 
+// One 16-element block: scale byte and 8 bytes of codes.
+__device__ __forceinline__ void quantize_block(u32x4 lo, u32x4 hi, bool degenerate, float s_enc,
+                                               float s_dec, u32x2& c, uint32_t& S) {
+  const u16x2 m = max_u16x2(max8(lo), max8(hi));
+  const float a_b = bf16_bits_to_f32(m.x > m.y ? m.x : m.y);
+  S = degenerate ? 0u : e4m3_from_f32_rne((a_b / 6.0f) * s_enc);
+  if (S == 0) {
+    c = u32x2{signs8(lo), signs8(hi)};
+  } else {
+    const float e = 1.0f / (e4m3_to_f32(S) * s_dec);
+    c = u32x2{encode8(lo, e), encode8(hi, e)};
+  }
+}
+
+// Every workgroup folds the amax words, derives s_enc / s_dec, then each
+// thread quantizes U blocks per round (all 2U loads issued first).
+template <int U>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
-    const uint4* __restrict__ x, int64_t nblocks, const uint32_t* __restrict__ amax_words,
-    int n_amax, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+    const u32x4* __restrict__ x, int64_t nblocks, const uint32_t* __restrict__ amax_words,
+    int n_amax, u32x2* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ tensor_scale, int32_t* __restrict__ dev_status) {
   const uint32_t amax_bits = fold_amax_words(amax_words, n_amax);
   const bool first = blockIdx.x == 0 && threadIdx.x == 0;
@@ -125,26 +143,28 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
     *tensor_scale = s_dec;
     if (dev_status) *dev_status = 0;
   }
-  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; b < nblocks; b += stride) {
-    const uint4 lo = load_nt(x + 2 * b);
-    const uint4 hi = load_nt(x + 2 * b + 1);
-    u16x2 m = max_u16x2(max_u16x2(max_u16x2(abs_halves(lo.x), abs_halves(lo.y)),
-                                  max_u16x2(abs_halves(lo.z), abs_halves(lo.w))),
-                        max_u16x2(max_u16x2(abs_halves(hi.x), abs_halves(hi.y)),
-                                  max_u16x2(abs_halves(hi.z), abs_halves(hi.w))));
-    const float a_b = bf16_bits_to_f32(m.x > m.y ? m.x : m.y);
-    uint32_t S = 0;
-    if (!degenerate) S = e4m3_from_f32_rne((a_b / 6.0f) * s_enc);
-    uint2 c;
-    if (S == 0) {
-      c.x = signs8(lo);
-      c.y = signs8(hi);
-    } else {
-      const float e = 1.0f / (e4m3_to_f32(S) * s_dec);
-      c.x = encode8(lo, e);
-      c.y = encode8(hi, e);
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads * U;
+  int64_t b = (int64_t)blockIdx.x * kQuantThreads * U + threadIdx.x;
+  for (; b + (U - 1) * kQuantThreads < nblocks; b += stride) {
+    u32x4 lo[U], hi[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      lo[u] = __builtin_nontemporal_load(x + 2 * (b + u * kQuantThreads));
+      hi[u] = __builtin_nontemporal_load(x + 2 * (b + u * kQuantThreads) + 1);
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      u32x2 c;
+      uint32_t S;
+      quantize_block(lo[u], hi[u], degenerate, s_enc, s_dec, c, S);
+      codes[b + u * kQuantThreads] = c;
+      scales[b + u * kQuantThreads] = (uint8_t)S;
+    }
+  }
+  for (; b < nblocks; b += kQuantThreads) {
+    u32x2 c;
+    uint32_t S;
+    quantize_block(x[2 * b], x[2 * b + 1], degenerate, s_enc, s_dec, c, S);
     codes[b] = c;
     scales[b] = (uint8_t)S;
   }
@@ -189,6 +209,29 @@ static int grid_for(int64_t work, int per_thread, int cap) {
   return (int)g;
 }
 
+// Launch shape.  Defaults: the amax pass reads with 8 loads in flight per
+// thread over at most kMaxAmaxPartials workgroups; the quantizer handles 2
+// blocks per thread and round over at most 2048 workgroups, so every
+// workgroup's fold of the partials stays a small L2 read.
+struct QuantShape {
+  int amax_u = 8, quant_u = 2, quant_grid = 2048, amax_grid = kMaxAmaxPartials;
+};
+
+static QuantShape quant_shape() {
+  QuantShape q;
+  // debug pinning: "amax_u,amax_grid,quant_u,quant_grid"
+  if (const char* e = getenv("NVFP4_QUANT_SHAPE")) {
+    int a, ag, u, g;
+    if (sscanf(e, "%d,%d,%d,%d", &a, &ag, &u, &g) == 4) {
+      q.amax_u = a;
+      q.amax_grid = ag < kMaxAmaxPartials ? ag : kMaxAmaxPartials;
+      q.quant_u = u;
+      q.quant_grid = g;
+    }
+  }
+  return q;
+}
+
 int amax_partial_count(int64_t numel) {
   return grid_for(numel / 8, 8, kMaxAmaxPartials);
 }
@@ -196,26 +239,43 @@ int amax_partial_count(int64_t numel) {
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, float* tensor_scale, const float* amax_in,
                            uint32_t* workspace, int32_t* dev_status, hipStream_t stream) {
+  const QuantShape qs = quant_shape();
   const int64_t numel = rows * cols;
   const int64_t nblocks = numel / 16;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   const uint32_t* words;
   int n_words;
   if (amax_in) {
     words = reinterpret_cast<const uint32_t*>(amax_in);
     n_words = 1;
   } else {
-    const int g = amax_partial_count(numel);
-    hipLaunchKernelGGL(amax_partial_kernel, dim3(g), dim3(kQuantThreads), 0, stream,
-                       reinterpret_cast<const uint4*>(x), numel / 8, workspace);
+    int g = amax_partial_count(numel);
+    if (g > qs.amax_grid) g = qs.amax_grid;
+    const int64_t n16 = numel / 8;
+    const int64_t chunk = (n16 + g - 1) / g;
+    if (qs.amax_u == 4)
+      hipLaunchKernelGGL(amax_partial_kernel<4>, dim3(g), dim3(kQuantThreads), 0, stream, xv, n16, chunk, workspace);
+    else if (qs.amax_u == 16)
+      hipLaunchKernelGGL(amax_partial_kernel<16>, dim3(g), dim3(kQuantThreads), 0, stream, xv, n16, chunk, workspace);
+    else
+      hipLaunchKernelGGL(amax_partial_kernel<8>, dim3(g), dim3(kQuantThreads), 0, stream, xv, n16, chunk, workspace);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     words = workspace;
     n_words = g;
   }
-  const int g = grid_for(nblocks, 4, 4096);
-  hipLaunchKernelGGL(quantize_kernel, dim3(g), dim3(kQuantThreads), 0, stream,
-                     reinterpret_cast<const uint4*>(x), nblocks, words, n_words,
-                     reinterpret_cast<uint2*>(codes), scales, tensor_scale, dev_status);
+  const int u = qs.quant_u == 1 || qs.quant_u == 4 ? qs.quant_u : 2;
+  const int g = grid_for(nblocks, u, qs.quant_grid > 0 ? qs.quant_grid : 1 << 30);
+  u32x2* cv = reinterpret_cast<u32x2*>(codes);
+  if (u == 1)
+    hipLaunchKernelGGL(quantize_kernel<1>, dim3(g), dim3(kQuantThreads), 0, stream, xv, nblocks,
+                       words, n_words, cv, scales, tensor_scale, dev_status);
+  else if (u == 4)
+    hipLaunchKernelGGL(quantize_kernel<4>, dim3(g), dim3(kQuantThreads), 0, stream, xv, nblocks,
+                       words, n_words, cv, scales, tensor_scale, dev_status);
+  else
+    hipLaunchKernelGGL(quantize_kernel<2>, dim3(g), dim3(kQuantThreads), 0, stream, xv, nblocks,
+                       words, n_words, cv, scales, tensor_scale, dev_status);
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ Both then apply the same float64 epilogue and one bf16 rounding.
 """
 
 import numpy as np
-from scipy.special import erf
+from scipy.special import erfc
 
 from .formats import (E2M1_MAGNITUDES, bf16_bits_to_f64, e4m3_value,
                       round_to_bf16_bits)
@@ -50,9 +50,14 @@ def _block_values_int(codes, scales, cols):
 
 
 def gelu_f64(z):
-    """erf-form GELU, g(z) = z/2 * (1 + erf(z / sqrt 2)) (R-16), float64."""
+    """erf-form GELU, g(z) = z/2 * (1 + erf(z / sqrt 2)) (R-16), float64.
+
+    Evaluated as z/2 * erfc(-z / sqrt 2), the same function: 1 + erf(u) and
+    erfc(-u) are equal, but the erfc form keeps full relative accuracy in the
+    negative tail, where 1 + erf(u) cancels (it is wrong by 100% near z = -12).
+    """
     z = np.asarray(z, dtype=np.float64)
-    return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
+    return 0.5 * z * erfc(-z / np.sqrt(2.0))
 
 
 def epilogue_to_bf16(scaled, bias_bits=None, gelu=False):

@@ -17,7 +17,9 @@ import os
 import numpy as np
 import pytest
 
-from oracle.formats import E2M1_MAGNITUDES, e2m1_encode_magnitude, e4m3_encode_nonneg, e4m3_value
+from oracle.formats import (E2M1_MAGNITUDES, e2m1_encode_magnitude, e4m3_encode_nonneg,
+                            e4m3_value, round_to_bf16_bits)
+from oracle.gemm import gelu_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +38,7 @@ def probe():
     lib.nvfp4_probe_transitions.argtypes = [I, U, U, P, U, P, P, P]
     lib.nvfp4_probe_encode.argtypes = [I, P, I, P, P]
     lib.nvfp4_probe_decode.argtypes = [P, P, I, P, P, P, P, P]
+    lib.nvfp4_probe_bf16_gelu.argtypes = [P, I, P, P, P]
     return lib
 
 
@@ -171,3 +174,47 @@ def test_decodes_every_byte_and_scale(probe):
     want = e4m3_value(byte[scale_bytes].astype(np.uint8))
     for j in range(4):
         assert np.array_equal(s32[scale_bytes, j].view(np.uint32), want.view(np.uint32))
+
+
+def _bf16_gelu(lib, x):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    b = torch.zeros(len(x), dtype=torch.int16, device="cuda")
+    g = torch.zeros(len(x), dtype=torch.float32, device="cuda")
+    assert lib.nvfp4_probe_bf16_gelu(t.data_ptr(), len(x), b.data_ptr(), g.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    return b.cpu().numpy().view(np.uint16), g.cpu().numpy()
+
+
+def test_bf16_conversion_rounds_to_nearest_even(probe):
+    rng = np.random.default_rng(7)
+    parts = [rng.standard_normal(1 << 20).astype(np.float32),
+             np.exp(rng.uniform(-87, 88, 1 << 20)).astype(np.float32) * rng.choice([-1, 1], 1 << 20),
+             (rng.standard_normal(1 << 16) * 1e-39).astype(np.float32)]
+    # exact ties and their neighbours for every exponent: bf16 value + half its quantum
+    hi = (np.arange(1 << 16, dtype=np.uint32) << 16)
+    hi = hi[((hi >> 23) & 0xFF) != 0xFF]
+    ties = hi | np.uint32(0x8000)
+    parts += [ties.view(np.float32), (ties + 1).view(np.float32), (ties - 1).view(np.float32)]
+    x = np.concatenate(parts)
+    if len(x) % 2:
+        x = x[:-1]
+    got, _ = _bf16_gelu(probe, x)
+    assert np.array_equal(got, round_to_bf16_bits(x))
+
+
+def test_gelu_matches_oracle(probe):
+    z = np.concatenate([np.linspace(-40, 40, 400002), np.random.default_rng(8).standard_normal(100000) * 3])
+    z = z.astype(np.float32)
+    _, g = _bf16_gelu(probe, z)
+    ref = gelu_f64(z.astype(np.float64))
+    # relative error well below a bf16 ulp (2^-8): ~1e-6 where exp's argument is
+    # small (a few binary32 ulps of the reciprocal, the Horner steps and exp2); in the
+    # far tail binary32 rounding of x^2 and of the exponent
+    # argument (|arg| up to 800 at |z| = 40) limits it to a few 1e-5
+    big = np.abs(ref) > 1e-30
+    rel = np.abs(g - ref) / np.where(big, np.abs(ref), 1.0)
+    near = np.abs(z) <= 4
+    assert rel[near & big].max() < 5e-6, rel[near & big].max()
+    assert rel[big].max() < 5e-5, rel[big].max()
+    assert np.all(np.abs(g[~big]) <= 1e-30)

@@ -130,6 +130,9 @@ def test_gelu_pins():
     assert gelu_f64(np.array([0.0]))[0] == 0.0
     assert np.allclose(gelu_f64(z) - gelu_f64(-z), z, rtol=0, atol=1e-14)
     assert np.allclose(gelu_f64(z), z * norm.cdf(z), rtol=1e-13, atol=1e-15)
+    # the negative tail keeps relative accuracy (no cancellation)
+    zt = np.linspace(-30, -5, 1001)
+    assert np.allclose(gelu_f64(zt), zt * norm.cdf(zt), rtol=1e-12, atol=0)
     assert abs(gelu_f64(np.array([1.0]))[0] - 0.8413447460685429) < 1e-15
 
 
