@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-rows", type=int, default=6144)
+    p.add_argument("--cpu-rows", type=int, default=12288)
     p.add_argument("--calib-copy", action="store_true")
     return p.parse_args()
 

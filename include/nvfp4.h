@@ -148,8 +148,7 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
  *   bias_bf16         optional [N] bf16.
  *   M, N >= 0; K > 0, K % 16 == 0.  Code pointers 8-byte aligned.
  *   epilogue          an nvfp4_epilogue value.
- *   y_bf16            out [M, N] bf16, 4-byte aligned; N % 2 == 0 is not
- *                     required.
+ *   y_bf16            out [M, N] bf16, 2-byte aligned; any N >= 0.
  *   y_amax            optional device float: set to max |Y| over the bf16
  *                     outputs (the call zeroes it first, on `stream`), ready
  *                     to be passed as amax_in of the next nvfp4_quantize.
@@ -164,7 +163,7 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_t
  * ([P1] "NVFP4量化": chosen layers keep their original precision):
  *   Y[m,n] = bf16_rne( epi( sum_k X[m,k] * W[n,k] + bias[n] ) ), fp32 accumulation.
  *   x_bf16 [M, K], w_bf16 [N, K], bias_bf16 optional [N], y_bf16 [M, N];
- *   M, N >= 0, K > 0, K % 8 == 0; x / w 16-byte aligned, y 4-byte aligned.
+ *   M, N >= 0, K > 0, K % 8 == 0; x / w 16-byte aligned, bias / y 2-byte aligned.
  */
 int nvfp4_gemm_bf16(const void* x_bf16, const void* w_bf16, const void* bias_bf16,
                     int64_t M, int64_t N, int64_t K, int epilogue, void* y_bf16,
