@@ -128,9 +128,11 @@ def main():
     ws = torch.empty(nv.quantize_workspace_bytes(TOKENS, HIDDEN), dtype=torch.uint8, device=dev)
     xq = nv.quantize(x, workspace=ws)
     amax = torch.empty(1, dtype=torch.float32, device=dev)
-    h = nv.gemm(xq, wq_up, epilogue="gelu", y_amax=amax)
+    ws_up = nv.gemm_workspace(TOKENS, MLP, HIDDEN, device=dev)      # K-split of the tail tiles
+    ws_down = nv.gemm_workspace(TOKENS, HIDDEN, MLP, device=dev)
+    h = nv.gemm(xq, wq_up, epilogue="gelu", y_amax=amax, workspace=ws_up)
     hq = nv.quantize(h, amax=amax)
-    y = nv.gemm(hq, wq_down)
+    y = nv.gemm(hq, wq_down, workspace=ws_down)
     xq_out = (xq.codes, xq.scales, xq.tensor_scale)
     hq_out = (hq.codes, hq.scales, hq.tensor_scale)
 
@@ -142,13 +144,13 @@ def main():
         nv.quantize(x, workspace=ws, out=xq_out)
         if events is not None:
             events[1].record(stream)
-        nv.gemm(xq, wq_up, epilogue="gelu", y_amax=amax, out=h)
+        nv.gemm(xq, wq_up, epilogue="gelu", y_amax=amax, out=h, workspace=ws_up)
         if events is not None:
             events[2].record(stream)
         nv.quantize(h, amax=amax, out=hq_out)
         if events is not None:
             events[3].record(stream)
-        nv.gemm(hq, wq_down, out=y)
+        nv.gemm(hq, wq_down, out=y, workspace=ws_down)
         if events is not None:
             events[4].record(stream)
 

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 #define NVFP4_BLOCK 16 /* elements per block scale, [P1] "NVFP4量化" */
 
 typedef enum {
@@ -152,11 +152,29 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
  *   y_amax            optional device float: set to max |Y| over the bf16
  *                     outputs (the call zeroes it first, on `stream`), ready
  *                     to be passed as amax_in of the next nvfp4_quantize.
+ *   workspace         optional device scratch, 256-byte aligned, owned by the
+ *                     call until it completes on `stream`; contents on entry
+ *                     irrelevant.  With at least nvfp4_gemm_workspace_bytes
+ *                     (M, N, K) bytes the tiles that do not fill a whole round
+ *                     of workgroups over the compute units are split over K
+ *                     and their fp32 partial sums added there, in a fixed
+ *                     order, by a second kernel on `stream`; NULL or a
+ *                     smaller size computes every tile whole.  Either way the
+ *                     result is deterministic; the two differ only in the
+ *                     order of the fp32 additions.
  */
 int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                const uint8_t* w_codes, const uint8_t* w_scales, const float* w_tensor_scale,
                const void* bias_bf16, int64_t M, int64_t N, int64_t K, int epilogue,
-               void* y_bf16, float* y_amax, void* stream);
+               void* y_bf16, float* y_amax, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
+ * nvfp4_gemm_workspace_bytes -- workspace bytes nvfp4_gemm can use for an
+ * (M, N, K) problem on the current device (0: it would not split).  Host
+ * only; at most 256 KiB per compute unit (64 MiB on a 256-CU device).
+ */
+size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * nvfp4_gemm_bf16 -- the bf16 passthrough for layers kept in higher precision

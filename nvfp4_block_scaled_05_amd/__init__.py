@@ -83,17 +83,37 @@ def dequantize(q, out=None):
     return y
 
 
-def gemm(a, w, bias=None, epilogue="none", y_amax=None, out=None):
-    """Y = epi(sA*sW * A_hat @ W_hat^T + bias) in bf16, from two ``Nvfp4Tensor``."""
+def gemm_workspace(M, N, K, device="cuda"):
+    """A workspace for ``gemm`` on an (M, N, K) problem, or None if it would not split."""
+    nbytes = load().nvfp4_gemm_workspace_bytes(M, N, K)
+    if nbytes == 0:
+        return None
+    return _torch().empty(nbytes, dtype=_torch().uint8, device=device)
+
+
+_NO_WORKSPACE = object()
+
+
+def gemm(a, w, bias=None, epilogue="none", y_amax=None, out=None, workspace=_NO_WORKSPACE):
+    """Y = epi(sA*sW * A_hat @ W_hat^T + bias) in bf16, from two ``Nvfp4Tensor``.
+
+    ``workspace``: a uint8 device tensor from ``gemm_workspace`` (reused across
+    calls on one stream), None to compute every tile whole, or left out to have
+    one taken from torch's caching allocator for this call.
+    """
     torch = _torch()
     M, N, K = a.codes.shape[0], w.codes.shape[0], a.cols
     if w.cols != K:
         raise ValueError("K mismatch")
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.codes.device)
+    if workspace is _NO_WORKSPACE:
+        workspace = gemm_workspace(M, N, K, device=a.codes.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _binding.check(load().nvfp4_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(a.tensor_scale),
                                      _ptr(w.codes), _ptr(w.scales), _ptr(w.tensor_scale),
                                      _ptr(bias), M, N, K, EPILOGUES[epilogue], _ptr(y),
-                                     _ptr(y_amax), _stream()), "nvfp4_gemm")
+                                     _ptr(y_amax), _ptr(workspace), ws_bytes, _stream()),
+                   "nvfp4_gemm")
     return y
 
 

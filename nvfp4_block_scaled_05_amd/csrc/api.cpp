@@ -108,10 +108,15 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
                                              static_cast<hipStream_t>(stream)));
 }
 
+size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K) || K % 16 != 0) return 0;
+  return nvfp4::gemm_nvfp4_workspace_bytes(M, N, K);
+}
+
 int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                const uint8_t* w_codes, const uint8_t* w_scales, const float* w_tensor_scale,
                const void* bias_bf16, int64_t M, int64_t N, int64_t K, int epilogue, void* y_bf16,
-               float* y_amax, void* stream) {
+               float* y_amax, void* workspace, size_t workspace_bytes, void* stream) {
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return NVFP4_ERR_SHAPE;
   const bool empty = M == 0 || N == 0;
   if (!empty && (!a_codes || !a_scales || !a_tensor_scale || !w_codes || !w_scales ||
@@ -121,14 +126,15 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_t
   if (((M + 127) / 128) * ((N + 127) / 128) >= ((int64_t)1 << 24)) return NVFP4_ERR_SHAPE;
   if (!aligned(a_codes, 8) || !aligned(w_codes, 8) || !aligned(a_tensor_scale, 4) ||
       !aligned(w_tensor_scale, 4) || !aligned(bias_bf16, 2) || !aligned(y_bf16, 2) ||
-      !aligned(y_amax, 4))
+      !aligned(y_amax, 4) || !aligned(workspace, 256))
     return NVFP4_ERR_ALIGN;
   if (epilogue != NVFP4_EPI_NONE && epilogue != NVFP4_EPI_GELU) return NVFP4_ERR_ARG;
   int st = check_device();
   if (st != NVFP4_OK) return st;
   return hip_status(nvfp4::launch_gemm_nvfp4(a_codes, a_scales, a_tensor_scale, w_codes, w_scales,
                                              w_tensor_scale, bias_bf16, M, N, K, epilogue, y_bf16,
-                                             y_amax, static_cast<hipStream_t>(stream)));
+                                             y_amax, workspace, workspace ? workspace_bytes : 0,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int nvfp4_gemm_bf16(const void* x_bf16, const void* w_bf16, const void* bias_bf16, int64_t M,

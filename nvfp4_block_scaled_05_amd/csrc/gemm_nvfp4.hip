@@ -31,6 +31,7 @@
 //   * the tile order is renumbered so each XCD (workgroups are dealt to the 8
 //     XCDs round-robin) walks a contiguous, row-grouped range of tiles and
 //     reuses A and W panels in its own L2.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -304,16 +305,21 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::TM][C::TN], floa
   }
 }
 
-// Tile index of this workgroup: XCD-contiguous ranges, then row-grouped order.
-__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm,
-                                            int64_t& tn) {
-  const int64_t T = tiles_m * tiles_n;
-  const int64_t b = blockIdx.x;
+// Position, in XCD-contiguous order, of workgroup b among the first T
+// workgroups: they are dealt to the XCDs round-robin, so the ones on XCD k
+// (b % 8 == k) take the k-th contiguous range of positions.
+__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t T) {
   const int64_t xcd = b % kXcds, slot = b / kXcds;
   // workgroups with id % 8 == k: n_k = ceil((T - k) / 8); start_k = sum_{j<k} n_j
   int64_t start = 0;
   for (int64_t k = 0; k < xcd; ++k) start += (T - k + kXcds - 1) / kXcds;
-  const int64_t t = start + slot;
+  return start + slot;
+}
+
+// Tile (tm, tn) at position t of the row-grouped order: groups of kGroupM
+// tile-rows, column-major inside a group, so neighbours share A and W panels.
+__device__ __forceinline__ void grouped_tile(int64_t t, int64_t tiles_m, int64_t tiles_n,
+                                             int64_t& tm, int64_t& tn) {
   const int64_t per_group = kGroupM * tiles_n;
   const int64_t group = t / per_group;
   const int64_t first_m = group * kGroupM;
@@ -321,6 +327,12 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
   const int64_t in_group = t - group * per_group;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
+}
+
+// Tile index of this workgroup: XCD-contiguous ranges, then row-grouped order.
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                            int64_t& tn) {
+  grouped_tile(xcd_order(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 template <class C>
@@ -438,92 +450,6 @@ __device__ __forceinline__ void store_stage2(const Staged2& s, uint8_t* stage) {
   d[3] = __builtin_bit_cast(u32x4, decode8(s.w.w, s1));
 }
 
-template <class C>
-__device__ __forceinline__ void compute_stage2(const uint8_t* stage, f32x16 (&acc)[C::TM][C::TN]) {
-  using L = Lay2<C>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / C::WGN, wn = wave % C::WGN;
-  const int r = lane & 31, h = lane >> 5;
-  u32x4 ca[C::TM];
-  f16x2 sa[C::TM];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
-    const int row = wm * C::WM + i * 32 + r;
-    ca[i] = *reinterpret_cast<const u32x4*>(stage + L::A_CODES + row * kACodePitch2 + h * 16);
-    sa[i] = *reinterpret_cast<const f16x2*>(stage + L::A_SC + row * kAScalePitch2 + h * 4);
-  }
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    f16x8 av[C::TM], bv[C::TN];
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int row = wn * C::WN + j * 32 + r;
-      bv[j] = *reinterpret_cast<const f16x8*>(stage + L::W_F16 + row * kWPitch2 + (h * 32 + kk * 8) * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-      const uint32_t w = kk == 0 ? ca[i].x : kk == 1 ? ca[i].y : kk == 2 ? ca[i].z : ca[i].w;
-      av[i] = decode8(w, kk < 2 ? sa[i].x : sa[i].y);
-    }
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-template <class C, bool kEdge>
-__device__ __forceinline__ void main_loop2(const Operand& A, const Operand& Wt, int64_t m0,
-                                           int64_t n0, int64_t K, uint8_t* lds,
-                                           f32x16 (&acc)[C::TM][C::TN]) {
-  using L = Lay2<C>;
-  const int64_t kblocks = K / 16;
-  const int nk = (int)((K + kBK2 - 1) / kBK2);
-  Staged2 st;
-  load_stage2<C, kEdge>(A, Wt, m0, n0, 0, kblocks, st);
-  store_stage2<C>(st, lds);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    uint8_t* cur = lds + (kt & 1) * L::STAGE;
-    uint8_t* nxt = lds + ((kt + 1) & 1) * L::STAGE;
-    const int kn = kt + 1 < nk ? kt + 1 : kt;     // unconditional prefetch (see main_loop)
-    load_stage2<C, kEdge>(A, Wt, m0, n0, kn, kblocks, st);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_stage2<C>(cur, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    store_stage2<C>(st, nxt);
-    __syncthreads();
-  }
-}
-
-template <class C>
-__global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_wlds_kernel(
-    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
-    const float* __restrict__ sa, const uint8_t* __restrict__ w_codes,
-    const uint8_t* __restrict__ w_scales, const float* __restrict__ sw,
-    const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi,
-    uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax, int vec_flags) {
-  using L = Lay2<C>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::STAGE];
-  const int64_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
-  int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
-  const Operand A{a_codes, a_scales, M}, Wt{w_codes, w_scales, N};
-  f32x16 acc[C::TM][C::TN];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
-  const bool interior = m0 + C::BM <= M && n0 + C::BN <= N && K % kBK2 == 0 && (vec_flags & 4);
-  if (interior)
-    main_loop2<C, false>(A, Wt, m0, n0, K, lds, acc);
-  else
-    main_loop2<C, true>(A, Wt, m0, n0, K, lds, acc);
-  epilogue<C>(acc, (*sa) * (*sw), bias, epi, M, N, m0, n0, y, y_amax);
-}
-
 // v3: v2 with the work of one K step software-pipelined inside each wave --
 // the LDS reads and activation decode of MFMA step kk+1, and (in the second
 // half of the step) the next stage's stores and weight decode, are issued
@@ -617,25 +543,121 @@ __device__ __forceinline__ void compute_stage3(const uint8_t* stage, const Stage
   }
 }
 
+// Stages [kb, ke) of the K loop (a stage is 64 elements of K).
 template <class C, bool kEdge>
 __device__ __forceinline__ void main_loop3(const Operand& A, const Operand& Wt, int64_t m0,
-                                           int64_t n0, int64_t K, uint8_t* lds,
+                                           int64_t n0, int64_t K, int kb, int ke, uint8_t* lds,
                                            f32x16 (&acc)[C::TM][C::TN]) {
   using L = Lay2<C>;
   const int64_t kblocks = K / 16;
-  const int nk = (int)((K + kBK2 - 1) / kBK2);
   Staged2 st;
-  load_stage2<C, kEdge>(A, Wt, m0, n0, 0, kblocks, st);
+  load_stage2<C, kEdge>(A, Wt, m0, n0, kb, kblocks, st);
   store_stage2<C>(st, lds);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    uint8_t* cur = lds + (kt & 1) * L::STAGE;
-    uint8_t* nxt = lds + ((kt + 1) & 1) * L::STAGE;
-    const int kn = kt + 1 < nk ? kt + 1 : kt;
+  for (int kt = kb; kt < ke; ++kt) {
+    uint8_t* cur = lds + ((kt - kb) & 1) * L::STAGE;
+    uint8_t* nxt = lds + ((kt - kb + 1) & 1) * L::STAGE;
+    const int kn = kt + 1 < ke ? kt + 1 : kt;
     load_stage2<C, kEdge>(A, Wt, m0, n0, kn, kblocks, st);
     __builtin_amdgcn_sched_barrier(0);
     compute_stage3<C>(cur, st, nxt, acc);
     __syncthreads();
+  }
+}
+
+// Split K for the tail.  When the tiles do not fill a whole number of rounds
+// of workgroups over the compute units, the last, partial round leaves units
+// idle.  Its tiles are then each split into `ways` ranges of K stages given to
+// different workgroups, which store their fp32 partial sums, row-major, in
+// their own slice of the workspace; a second kernel adds the slices in split
+// order (the result does not depend on timing) and applies the epilogue.
+struct SplitK {
+  float* part;         // [tail tiles][ways][BM][BN] fp32 partial sums
+  int64_t main_tiles;  // tiles computed whole, by workgroups 0 .. main_tiles-1
+  int ways;            // K ranges per tail tile (1: no split)
+};
+
+// Work of this workgroup: tile (tm, tn), and for a tail tile its index among
+// the tail tiles and its split (split < 0 for a whole tile).
+__device__ __forceinline__ void split_coords(int64_t tiles_m, int64_t tiles_n, const SplitK& sk,
+                                             int64_t& tm, int64_t& tn, int64_t& tail,
+                                             int& split) {
+  const int64_t b = blockIdx.x;
+  if (b < sk.main_tiles) {
+    grouped_tile(xcd_order(b, sk.main_tiles), tiles_m, tiles_n, tm, tn);
+    tail = -1;
+    split = -1;
+  } else {
+    const int64_t u = b - sk.main_tiles;
+    tail = u / sk.ways;
+    split = (int)(u - tail * sk.ways);
+    grouped_tile(sk.main_tiles + tail, tiles_m, tiles_n, tm, tn);
+  }
+}
+
+// This workgroup's partial sums into its slice, at their tile positions (the
+// accumulator layout of the epilogue).
+template <class C>
+__device__ __forceinline__ void store_partial(const f32x16 (&acc)[C::TM][C::TN], const SplitK& sk,
+                                              int64_t tail, int split) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  float* slice = sk.part + (tail * sk.ways + split) * (int64_t)(C::BM * C::BN);
+  float* base = slice + (wm * C::WM + (lane >> 5) * 4) * C::BN + wn * C::WN + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        base[(i * 32 + (e >> 2) * 8 + (e & 3)) * C::BN + j * 32] = acc[i][j][e];
+}
+
+// Sums the slices of the tail tiles in split order and applies the epilogue
+// of the whole tiles (same operations, same order).  One thread per 4
+// consecutive outputs of a tile row; BM*BN/1024 workgroups per tail tile.
+template <class C>
+__global__ __launch_bounds__(256) void split_reduce_kernel(
+    const float* __restrict__ part, int64_t main_tiles, int ways, const float* __restrict__ sa,
+    const float* __restrict__ sw, const uint16_t* __restrict__ bias, int64_t M, int64_t N,
+    int epi, uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax) {
+  constexpr int kPerTile = C::BM * C::BN / 1024;
+  const int64_t tail = blockIdx.x / kPerTile;
+  const int q = (int)(blockIdx.x % kPerTile) * 256 + threadIdx.x;
+  const int r = q / (C::BN / 4), c = (q % (C::BN / 4)) * 4;
+  const int64_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
+  int64_t tm, tn;
+  grouped_tile(main_tiles + tail, tiles_m, tiles_n, tm, tn);
+  const int64_t row = tm * C::BM + r, col = tn * C::BN + c;
+  const float scale = (*sa) * (*sw);
+  const f32x4* src = reinterpret_cast<const f32x4*>(part + tail * ways * (int64_t)(C::BM * C::BN) +
+                                                    r * C::BN + c);
+  f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int w = 0; w < ways; ++w) sum += src[w * (C::BM * C::BN / 4)];
+  float amax = 0.0f;
+  if (row < M) {
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool ok = col + k < N;
+      const float bv = (bias && ok) ? bf16_bits_to_f32(bias[col + k]) : 0.0f;
+      v[k] = __builtin_fmaf(sum[k], scale, bv);
+      if (epi == 1) v[k] = gelu_erf(v[k]);
+    }
+    const uint32_t p01 = bf16x2_rne(v[0], v[1]), p23 = bf16x2_rne(v[2], v[3]);
+    const uint16_t h[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
+    uint16_t* dst = y + row * N + col;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (col + k < N) {
+        dst[k] = h[k];
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(v[k]));
+      }
+  }
+  if (y_amax) {
+    uint32_t a = (bf16x2_rne(amax, 0.0f) & 0xFFFFu) << 16;
+    a = wave_max_u32(a);
+    if ((threadIdx.x & 63) == 0) atomicMax(y_amax, a);
   }
 }
 
@@ -645,14 +667,18 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_pipe_kernel(
     const float* __restrict__ sa, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ sw,
     const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi,
-    uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax, int vec_flags) {
+    uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax, int vec_flags, SplitK sk) {
   using L = Lay2<C>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::STAGE];
   const int64_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
-  int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  int64_t tm, tn, tail;
+  int split;
+  split_coords(tiles_m, tiles_n, sk, tm, tn, tail, split);
   const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
   const Operand A{a_codes, a_scales, M}, Wt{w_codes, w_scales, N};
+  const int nk = (int)((K + kBK2 - 1) / kBK2);
+  const int kb = split < 0 ? 0 : (int)((int64_t)split * nk / sk.ways);
+  const int ke = split < 0 ? nk : (int)((int64_t)(split + 1) * nk / sk.ways);
   f32x16 acc[C::TM][C::TN];
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
@@ -660,9 +686,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_pipe_kernel(
     for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
   const bool interior = m0 + C::BM <= M && n0 + C::BN <= N && K % kBK2 == 0 && (vec_flags & 4);
   if (interior)
-    main_loop3<C, false>(A, Wt, m0, n0, K, lds, acc);
+    main_loop3<C, false>(A, Wt, m0, n0, K, kb, ke, lds, acc);
   else
-    main_loop3<C, true>(A, Wt, m0, n0, K, lds, acc);
+    main_loop3<C, true>(A, Wt, m0, n0, K, kb, ke, lds, acc);
+  if (split >= 0) {
+    store_partial<C>(acc, sk, tail, split);
+    return;
+  }
   epilogue<C>(acc, (*sa) * (*sw), bias, epi, M, N, m0, n0, y, y_amax);
 }
 
@@ -685,75 +715,111 @@ hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   return hipGetLastError();
 }
 
-template <class C, bool kPipe>
-hipError_t launch_tile2(const uint8_t* a_codes, const uint8_t* a_scales, const float* sa,
-                        const uint8_t* w_codes, const uint8_t* w_scales, const float* sw,
-                        const void* bias, int64_t M, int64_t N, int64_t K, int epi, void* y,
-                        uint32_t* amax, hipStream_t stream) {
-  const int64_t tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+using CfgPipe = Cfg<256, 256, 4, 2, 1>;    // 8 waves of 64x128 (v3)
+using CfgSmall = Cfg<128, 128, 2, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU (v1)
+
+// DiT-sized problems run v3 on 256x256 tiles; small ones v1 on 128x128 tiles,
+// two workgroups per CU.  NVFP4_GEMM_KERNEL=small|pipe pins one (testing).
+bool use_pipe(int64_t M, int64_t N) {
+  if (const char* f = getenv("NVFP4_GEMM_KERNEL")) {
+    if (!strcmp(f, "pipe")) return true;
+    if (!strcmp(f, "small")) return false;
+  }
+  return M * N > (int64_t)256 * 256 * 128;
+}
+
+int compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+struct SplitPlan {
+  int64_t tiles = 0;        // all tiles
+  int64_t main_tiles = 0;   // tiles computed whole
+  int64_t tail = 0;         // tiles split over K
+  int ways = 1;
+  size_t bytes = 0;         // workspace needed
+};
+
+// Tail split for the v3 kernel: the tiles past the last whole round of
+// workgroups over the compute units are split into `ways` K ranges of at least
+// 4 stages, as many as fill the round.  NVFP4_GEMM_SPLIT=n forces n ways on
+// the tail (testing).
+SplitPlan plan_split(int64_t M, int64_t N, int64_t K) {
+  using C = CfgPipe;
+  SplitPlan p;
+  p.tiles = p.main_tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  if (p.tiles == 0) return p;
+  const int cus = compute_units();
+  const int64_t nk = (K + kBK2 - 1) / kBK2;
+  const int64_t tail = p.tiles % cus;
+  if (tail == 0) return p;
+  int64_t ways = std::min<int64_t>(cus / tail, nk / 4);
+  if (const char* f = getenv("NVFP4_GEMM_SPLIT")) ways = std::min<int64_t>(atoi(f), nk);
+  if (ways < 2) return p;
+  p.tail = tail;
+  p.main_tiles = p.tiles - tail;
+  p.ways = (int)ways;
+  p.bytes = (size_t)tail * ways * C::BM * C::BN * sizeof(float);
+  return p;
+}
+
+hipError_t launch_pipe(const uint8_t* a_codes, const uint8_t* a_scales, const float* sa,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* sw,
+                       const void* bias, int64_t M, int64_t N, int64_t K, int epi, void* y,
+                       uint32_t* amax, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  using C = CfgPipe;
   const uintptr_t cal = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(w_codes);
   const uintptr_t sal = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(w_scales);
   // interior fast path: 16-byte code rows, 4-byte scale rows
   const bool vec = (K % 64 == 0) && (cal & 15) == 0 && (sal & 3) == 0;
-  if constexpr (kPipe)
-    hipLaunchKernelGGL((gemm_nvfp4_pipe_kernel<C>), dim3((unsigned)tiles), dim3(C::NT), 0, stream,
-                       a_codes, a_scales, sa, w_codes, w_scales, sw,
-                       reinterpret_cast<const uint16_t*>(bias), M, N, K, epi,
-                       reinterpret_cast<uint16_t*>(y), amax, vec ? 4 : 0);
-  else
-    hipLaunchKernelGGL((gemm_nvfp4_wlds_kernel<C>), dim3((unsigned)tiles), dim3(C::NT), 0, stream,
-                       a_codes, a_scales, sa, w_codes, w_scales, sw,
-                       reinterpret_cast<const uint16_t*>(bias), M, N, K, epi,
-                       reinterpret_cast<uint16_t*>(y), amax, vec ? 4 : 0);
+  const SplitPlan plan = plan_split(M, N, K);
+  const bool split = plan.ways > 1 && workspace && workspace_bytes >= plan.bytes;
+  const SplitK sk = split ? SplitK{static_cast<float*>(workspace), plan.main_tiles, plan.ways}
+                          : SplitK{nullptr, plan.tiles, 1};
+  const int64_t grid = split ? plan.main_tiles + plan.tail * plan.ways : plan.tiles;
+  hipLaunchKernelGGL((gemm_nvfp4_pipe_kernel<C>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
+                     a_codes, a_scales, sa, w_codes, w_scales, sw,
+                     reinterpret_cast<const uint16_t*>(bias), M, N, K, epi,
+                     reinterpret_cast<uint16_t*>(y), amax, vec ? 4 : 0, sk);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  hipLaunchKernelGGL((split_reduce_kernel<C>), dim3((unsigned)(plan.tail * (C::BM * C::BN / 1024))),
+                     dim3(256), 0, stream, static_cast<const float*>(workspace), plan.main_tiles,
+                     plan.ways, sa, sw, reinterpret_cast<const uint16_t*>(bias), M, N, epi,
+                     reinterpret_cast<uint16_t*>(y), amax);
   return hipGetLastError();
 }
 
-using Cfg256x256w4 = Cfg<256, 256, 2, 2, 1>;   // 4 waves of 128x128
-using Cfg256x256w8 = Cfg<256, 256, 2, 4, 1>;   // 8 waves of 128x64
-using Cfg256x256w8t = Cfg<256, 256, 4, 2, 1>;  // 8 waves of 64x128
-using Cfg256x128w4 = Cfg<256, 128, 2, 2, 1>;   // 4 waves of 128x64
-using Cfg256x128w8 = Cfg<256, 128, 4, 2, 1>;   // 8 waves of 64x64
-using Cfg128x128w4 = Cfg<128, 128, 2, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU
-
 }  // namespace
+
+size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || !use_pipe(M, N)) return 0;
+  return plan_split(M, N, K).bytes;
+}
 
 hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales,
                              const float* a_tensor_scale, const uint8_t* w_codes,
                              const uint8_t* w_scales, const float* w_tensor_scale,
                              const void* bias, int64_t M, int64_t N, int64_t K, int epilogue,
-                             void* y, float* y_amax, hipStream_t stream) {
+                             void* y, float* y_amax, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
   uint32_t* amax = reinterpret_cast<uint32_t*>(y_amax);
   if (amax) {
     hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, stream, amax);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (M == 0 || N == 0) return hipSuccess;
-  // DiT-sized problems: 256x256 tiles, 8 waves (two per SIMD), the weight
-  // decoded once per workgroup into LDS and the per-wave work software-
-  // pipelined (v3).  Small problems: 128x128 tiles, two workgroups per CU.
-  int choice = 5;
-  if (M * N > (int64_t)256 * 256 * 128) choice = 7;
-  const char* force = getenv("NVFP4_GEMM_CFG");   // debug pinning of the tile configuration
-  if (force && force[0] >= '0' && force[0] <= '7') choice = force[0] - '0';
-#define NVFP4_LAUNCH(CFG)                                                                     \
-  return launch_tile<CFG>(a_codes, a_scales, a_tensor_scale, w_codes, w_scales, w_tensor_scale, \
-                          bias, M, N, K, epilogue, y, amax, stream)
-  switch (choice) {
-    case 0: NVFP4_LAUNCH(Cfg256x256w4);
-    case 1: NVFP4_LAUNCH(Cfg256x256w8);
-    case 2: NVFP4_LAUNCH(Cfg256x256w8t);
-    case 3: NVFP4_LAUNCH(Cfg256x128w4);
-    case 4: NVFP4_LAUNCH(Cfg256x128w8);
-    case 6:
-      return launch_tile2<Cfg256x256w8t, false>(a_codes, a_scales, a_tensor_scale, w_codes, w_scales,
-                                                w_tensor_scale, bias, M, N, K, epilogue, y, amax, stream);
-    case 7:
-      return launch_tile2<Cfg256x256w8t, true>(a_codes, a_scales, a_tensor_scale, w_codes, w_scales,
-                                               w_tensor_scale, bias, M, N, K, epilogue, y, amax, stream);
-    default: NVFP4_LAUNCH(Cfg128x128w4);
-  }
-#undef NVFP4_LAUNCH
+  if (use_pipe(M, N))
+    return launch_pipe(a_codes, a_scales, a_tensor_scale, w_codes, w_scales, w_tensor_scale, bias, M,
+                       N, K, epilogue, y, amax, workspace, workspace_bytes, stream);
+  return launch_tile<CfgSmall>(a_codes, a_scales, a_tensor_scale, w_codes, w_scales,
+                               w_tensor_scale, bias, M, N, K, epilogue, y, amax, stream);
 }
 
 }  // namespace nvfp4

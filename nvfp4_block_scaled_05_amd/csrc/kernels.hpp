@@ -23,7 +23,12 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales,
                              const float* a_tensor_scale, const uint8_t* w_codes,
                              const uint8_t* w_scales, const float* w_tensor_scale,
                              const void* bias, int64_t M, int64_t N, int64_t K, int epilogue,
-                             void* y, float* y_amax, hipStream_t stream);
+                             void* y, float* y_amax, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+// Workspace bytes launch_gemm_nvfp4 can use to split the tail tiles over K
+// (0: no split for this shape).
+size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, int64_t M, int64_t N,
                             int64_t K, int epilogue, void* y, hipStream_t stream);

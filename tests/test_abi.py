@@ -34,14 +34,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(lib, n), n
         assert n in _binding.SIGNATURES, n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.nvfp4_abi_version() == 1
+    assert lib.nvfp4_abi_version() == 2
     for code in range(-8, 1):
         assert lib.nvfp4_status_string(code)
     assert lib.nvfp4_status_string(-99) == b"unknown status"
@@ -93,8 +93,23 @@ def test_dequantize_argument_errors(lib):
     assert d(A + 4, A, A, 4, 32, A, None) == ALIGN
 
 
-def g(lib, M=64, N=64, K=64, epi=0, y=A, bias=None, amax=None, ac=A, wc=A):
-    return lib.nvfp4_gemm(ac, A, A, wc, A, A, bias, M, N, K, epi, y, amax, None)
+def g(lib, M=64, N=64, K=64, epi=0, y=A, bias=None, amax=None, ac=A, wc=A, ws=None, wsb=0):
+    return lib.nvfp4_gemm(ac, A, A, wc, A, A, bias, M, N, K, epi, y, amax, ws, wsb, None)
+
+
+def test_gemm_workspace_bytes(lib):
+    wb = lib.nvfp4_gemm_workspace_bytes
+    # invalid shapes and small problems (128x128 tiles) never split
+    assert wb(0, 64, 64) == wb(-1, 64, 64) == wb(64, 64, 40) == 0
+    assert wb(128, 1024, 1024) == 0
+    # DiT MLP projections at 2048^2 with a CFG pair: the tiles past the last
+    # whole round over the compute units are split over K
+    down = wb(16896, 3072, 12288)
+    up = wb(16896, 12288, 3072)
+    assert 0 < up and 0 < down <= 64 << 20
+    assert down % (256 * 1024) == 0 and up % (256 * 1024) == 0
+    # a whole number of rounds: nothing to split
+    assert wb(256 * 16, 256 * 16, 4096) == 0
 
 
 def test_gemm_argument_errors(lib):
@@ -105,6 +120,7 @@ def test_gemm_argument_errors(lib):
     assert g(lib, ac=A + 4) == ALIGN
     assert g(lib, y=A + 1) == ALIGN
     assert g(lib, amax=A + 2) == ALIGN
+    assert g(lib, ws=A + 16, wsb=1 << 20) == ALIGN
     assert g(lib, epi=7) == ARG
     b = lib.nvfp4_gemm_bf16
     assert b(None, A, None, 8, 8, 64, 0, A, None) == NULL

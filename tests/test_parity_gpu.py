@@ -337,6 +337,42 @@ def test_gemm_deterministic():
     assert np.array_equal(y1, y2)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 520, 1088), (257, 300, 1040), (64, 33, 3072)])
+@pytest.mark.parametrize("kernel,split", [("small", None), ("pipe", None), ("pipe", "3"),
+                                          ("pipe", "7")])
+def test_gemm_kernels_and_k_split(monkeypatch, M, N, K, kernel, split):
+    # every kernel path on ragged tiles: 128x128 tiles, 256x256 tiles whole,
+    # and 256x256 tiles with their K range split over 3 or 7 workgroups
+    monkeypatch.setenv("NVFP4_GEMM_KERNEL", kernel)
+    if split:
+        monkeypatch.setenv("NVFP4_GEMM_SPLIT", split)
+        assert nv.gemm_workspace(M, N, K) is not None
+    y, ref = _gemm_case(M, N, K, seed=M + 3 * N + K, epilogue="gelu" if split == "7" else "none")
+    assert_gemm_close(y, ref, f"{kernel}/{split} {M}x{N}x{K}")
+
+
+def test_gemm_k_split_deterministic_with_amax(monkeypatch):
+    import torch
+    monkeypatch.setenv("NVFP4_GEMM_KERNEL", "pipe")
+    monkeypatch.setenv("NVFP4_GEMM_SPLIT", "5")
+    M, N, K = 520, 300, 2048
+    a_bits = W.random_matrix(81, (M, K), "t3")
+    w_bits = W.random_matrix(82, (N, K), "normal", 0.02)
+    qa, ra = check_quantize(a_bits)
+    qw, rw = check_quantize(w_bits)
+    ws = nv.gemm_workspace(M, N, K)
+    amax = torch.full((1,), 1e30, dtype=torch.float32, device="cuda")
+    y1 = bits_of(nv.gemm(qa, qw, epilogue="gelu", y_amax=amax, workspace=ws))
+    assert np.float32(amax.item()) == np.abs(bf16_bits_to_f32(y1)).max()
+    y2 = bits_of(nv.gemm(qa, qw, epilogue="gelu", workspace=ws))     # same workspace reused
+    assert np.array_equal(y1, y2)
+    whole = bits_of(nv.gemm(qa, qw, epilogue="gelu", workspace=None))
+    ref, _ = gemm_fp64(ra, rw, K, gelu=True)
+    assert_gemm_close(y1, ref, "split")
+    assert_gemm_close(whole, ref, "whole")
+    assert float((ulp_diff(y1, whole) > 1).mean()) <= 1e-3   # only the fp32 addition order differs
+
+
 # ------------------------------------------------------- bf16 passthrough --
 
 @pytest.mark.parametrize("M,N,K", [(64, 64, 64), (130, 70, 40), (2, 1000, 3072), (300, 257, 1024)])
