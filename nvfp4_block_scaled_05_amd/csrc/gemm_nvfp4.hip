@@ -298,10 +298,18 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::TM][C::TN], floa
         }
       }
   }
-  if (y_amax) {
+  if (y_amax) {   // one atomic per workgroup
+    __shared__ uint32_t wave_amax[C::NT / 64];
     uint32_t a = (bf16x2_rne(amax, 0.0f) & 0xFFFFu) << 16;
     a = wave_max_u32(a);
-    if (lane == 0) atomicMax(y_amax, a);
+    if (lane == 0) wave_amax[wave] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int w = 0; w < C::NT / 64; ++w) m = max(m, wave_amax[w]);
+      atomicMax(y_amax, m);
+    }
   }
 }
 
@@ -614,34 +622,44 @@ __device__ __forceinline__ void store_partial(const f32x16 (&acc)[C::TM][C::TN],
 }
 
 // Sums the slices of the tail tiles in split order and applies the epilogue
-// of the whole tiles (same operations, same order).  One thread per 4
-// consecutive outputs of a tile row; BM*BN/1024 workgroups per tail tile.
+// of the whole tiles (same operations, same order).  A workgroup covers
+// kReduceRows rows of a tile, each thread 4 consecutive outputs of a row per
+// step; the output amax is reduced in the workgroup first, so the amax word
+// sees one atomic per workgroup rather than a burst of one per wave.
+constexpr int kReduceRows = 64;
+
 template <class C>
 __global__ __launch_bounds__(256) void split_reduce_kernel(
     const float* __restrict__ part, int64_t main_tiles, int ways, const float* __restrict__ sa,
     const float* __restrict__ sw, const uint16_t* __restrict__ bias, int64_t M, int64_t N,
     int epi, uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax) {
-  constexpr int kPerTile = C::BM * C::BN / 1024;
+  constexpr int kPerTile = C::BM / kReduceRows;
+  constexpr int kCols4 = C::BN / 4;              // threads per tile row
+  constexpr int kRowStep = 256 / kCols4;         // rows per step
+  static_assert(256 % kCols4 == 0 && kReduceRows % kRowStep == 0, "reduce layout");
   const int64_t tail = blockIdx.x / kPerTile;
-  const int q = (int)(blockIdx.x % kPerTile) * 256 + threadIdx.x;
-  const int r = q / (C::BN / 4), c = (q % (C::BN / 4)) * 4;
+  const int r0 = (int)(blockIdx.x % kPerTile) * kReduceRows + threadIdx.x / kCols4;
+  const int c = (threadIdx.x % kCols4) * 4;
   const int64_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
   int64_t tm, tn;
   grouped_tile(main_tiles + tail, tiles_m, tiles_n, tm, tn);
-  const int64_t row = tm * C::BM + r, col = tn * C::BN + c;
+  const int64_t col = tn * C::BN + c;
   const float scale = (*sa) * (*sw);
-  const f32x4* src = reinterpret_cast<const f32x4*>(part + tail * ways * (int64_t)(C::BM * C::BN) +
-                                                    r * C::BN + c);
-  f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int w = 0; w < ways; ++w) sum += src[w * (C::BM * C::BN / 4)];
+  float bv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) bv[k] = (bias && col + k < N) ? bf16_bits_to_f32(bias[col + k]) : 0.0f;
+  const float* slices = part + tail * ways * (int64_t)(C::BM * C::BN);
   float amax = 0.0f;
-  if (row < M) {
+  for (int r = r0; r < r0 + kReduceRows; r += kRowStep) {
+    const int64_t row = tm * C::BM + r;
+    const f32x4* src = reinterpret_cast<const f32x4*>(slices + r * C::BN + c);
+    f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int w = 0; w < ways; ++w) sum += src[w * (C::BM * C::BN / 4)];
+    if (row >= M) continue;
     float v[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const bool ok = col + k < N;
-      const float bv = (bias && ok) ? bf16_bits_to_f32(bias[col + k]) : 0.0f;
-      v[k] = __builtin_fmaf(sum[k], scale, bv);
+      v[k] = __builtin_fmaf(sum[k], scale, bv[k]);
       if (epi == 1) v[k] = gelu_erf(v[k]);
     }
     const uint32_t p01 = bf16x2_rne(v[0], v[1]), p23 = bf16x2_rne(v[2], v[3]);
@@ -655,9 +673,15 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
       }
   }
   if (y_amax) {
+    __shared__ uint32_t wave_amax[4];
     uint32_t a = (bf16x2_rne(amax, 0.0f) & 0xFFFFu) << 16;
     a = wave_max_u32(a);
-    if ((threadIdx.x & 63) == 0) atomicMax(y_amax, a);
+    if ((threadIdx.x & 63) == 0) wave_amax[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t m = max(max(wave_amax[0], wave_amax[1]), max(wave_amax[2], wave_amax[3]));
+      atomicMax(y_amax, m);
+    }
   }
 }
 
@@ -746,8 +770,10 @@ struct SplitPlan {
 
 // Tail split for the v3 kernel: the tiles past the last whole round of
 // workgroups over the compute units are split into `ways` K ranges of at least
-// 4 stages, as many as fill the round.  NVFP4_GEMM_SPLIT=n forces n ways on
-// the tail (testing).
+// 4 stages, as many as fill the round.  Below 4 ways the partial-sum traffic
+// and the reduce kernel cost about what the split saves (measured on the DiT
+// up projection: 96 tail tiles, 2 ways), so the tail is computed whole.
+// NVFP4_GEMM_SPLIT=n forces n ways on the tail (testing).
 SplitPlan plan_split(int64_t M, int64_t N, int64_t K) {
   using C = CfgPipe;
   SplitPlan p;
@@ -758,6 +784,7 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K) {
   const int64_t tail = p.tiles % cus;
   if (tail == 0) return p;
   int64_t ways = std::min<int64_t>(cus / tail, nk / 4);
+  if (ways < 4) ways = 1;
   if (const char* f = getenv("NVFP4_GEMM_SPLIT")) ways = std::min<int64_t>(atoi(f), nk);
   if (ways < 2) return p;
   p.tail = tail;
@@ -788,7 +815,7 @@ hipError_t launch_pipe(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                      reinterpret_cast<uint16_t*>(y), amax, vec ? 4 : 0, sk);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
-  hipLaunchKernelGGL((split_reduce_kernel<C>), dim3((unsigned)(plan.tail * (C::BM * C::BN / 1024))),
+  hipLaunchKernelGGL((split_reduce_kernel<C>), dim3((unsigned)(plan.tail * (C::BM / kReduceRows))),
                      dim3(256), 0, stream, static_cast<const float*>(workspace), plan.main_tiles,
                      plan.ways, sa, sw, reinterpret_cast<const uint16_t*>(bias), M, N, epi,
                      reinterpret_cast<uint16_t*>(y), amax);
