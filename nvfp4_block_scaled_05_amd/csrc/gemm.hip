@@ -158,11 +158,95 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(
   epilogue(acc, 1.0f, bias, epi, M, N, m0, n0, y, nullptr);
 }
 
+// Few-row case (M <= kGemvMaxRows, e.g. the modulation linear on the timestep
+// embedding, M = 2): the weight read is the whole cost, so no tiles and no
+// MFMA.  Each wave owns kGemvRows weight rows; lane l reads 8 consecutive k
+// per 512-wide step of every row (16 B loads, a wave covers 1 KB of a row),
+// multiplies by the same k of every X row (L2-resident, read through the
+// cache), and accumulates in fp32; the 64 lanes' partial sums are then added
+// by a butterfly across the wave.
+static constexpr int kGemvMaxRows = 8;
+static constexpr int kGemvRows = 4;      // weight rows per wave
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int MR>
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const uint16_t* __restrict__ bias, int64_t N, int64_t K, int epi, uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kGemvRows;
+  if (n0 >= N) return;
+  float acc[kGemvRows][MR];
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[r][m] = 0.0f;
+  for (int64_t k = (int64_t)lane * 8; k < K; k += 512) {
+    u32x4 wv[kGemvRows], xv[MR];
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+      const int64_t n = n0 + r < N ? n0 + r : N - 1;
+      wv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w + n * K + k));
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) xv[m] = *reinterpret_cast<const u32x4*>(x + m * K + k);
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[r][m] = __builtin_fmaf(bf16_lo(wv[r][e]), bf16_lo(xv[m][e]), acc[r][m]);
+          acc[r][m] = __builtin_fmaf(bf16_hi(wv[r][e]), bf16_hi(xv[m][e]), acc[r][m]);
+        }
+  }
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) acc[r][m] += __shfl_xor(acc[r][m], off);
+  // lane r*MR + m writes output (m, n0 + r)
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+      if (lane == r * MR + m && n0 + r < N) {
+        float v = acc[r][m] + (bias ? bf16_bits_to_f32(bias[n0 + r]) : 0.0f);
+        if (epi == 1) v = gelu_erf(v);
+        y[m * N + n0 + r] = (uint16_t)bf16_rne_bits(v);
+      }
+}
+
+template <int MR>
+hipError_t launch_gemv(const void* x, const void* w, const void* bias, int64_t N, int64_t K,
+                       int epilogue, void* y, hipStream_t stream) {
+  const int64_t waves = (N + kGemvRows - 1) / kGemvRows;
+  hipLaunchKernelGGL((gemv_bf16_kernel<MR>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                     stream, reinterpret_cast<const uint16_t*>(x),
+                     reinterpret_cast<const uint16_t*>(w), reinterpret_cast<const uint16_t*>(bias),
+                     N, K, epilogue, reinterpret_cast<uint16_t*>(y));
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers --
 
 hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, int64_t M, int64_t N,
                             int64_t K, int epilogue, void* y, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  switch (M) {   // few rows: the weight-streaming kernel
+    case 1: return launch_gemv<1>(x, w, bias, N, K, epilogue, y, stream);
+    case 2: return launch_gemv<2>(x, w, bias, N, K, epilogue, y, stream);
+    case 3: return launch_gemv<3>(x, w, bias, N, K, epilogue, y, stream);
+    case 4: return launch_gemv<4>(x, w, bias, N, K, epilogue, y, stream);
+    case 5: return launch_gemv<5>(x, w, bias, N, K, epilogue, y, stream);
+    case 6: return launch_gemv<6>(x, w, bias, N, K, epilogue, y, stream);
+    case 7: return launch_gemv<7>(x, w, bias, N, K, epilogue, y, stream);
+    case 8: return launch_gemv<8>(x, w, bias, N, K, epilogue, y, stream);
+    default: break;
+  }
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)tiles), dim3(NT), 0, stream,
                      reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w),

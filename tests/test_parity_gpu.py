@@ -375,7 +375,8 @@ def test_gemm_k_split_deterministic_with_amax(monkeypatch):
 
 # ------------------------------------------------------- bf16 passthrough --
 
-@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (130, 70, 40), (2, 1000, 3072), (300, 257, 1024)])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (130, 70, 40), (2, 1000, 3072), (300, 257, 1024),
+                                   (1, 5, 8), (8, 777, 520), (7, 33, 4104), (9, 100, 256)])
 def test_gemm_bf16(M, N, K):
     x = W.random_matrix(M + N, (M, K), "normal")
     w = W.random_matrix(M + N + 1, (N, K), "normal", 0.02)
@@ -383,6 +384,17 @@ def test_gemm_bf16(M, N, K):
     y = bits_of(nv.gemm_bf16(to_dev(x), to_dev(w), bias=to_dev(b)))
     ref = linear_bf16_fp64(x, w, b)
     assert_gemm_close(y, ref, f"bf16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [2, 150])
+def test_gemm_bf16_gelu(M):
+    # both the few-row kernel and the tiled one apply the same epilogue
+    x = W.random_matrix(M, (M, 1024), "normal")
+    w = W.random_matrix(M + 1, (300, 1024), "normal", 0.05)
+    b = W.random_matrix(M + 2, (1, 300), "normal", 0.5)[0]
+    y = bits_of(nv.gemm_bf16(to_dev(x), to_dev(w), bias=to_dev(b), epilogue="gelu"))
+    ref = linear_bf16_fp64(x, w, b, gelu=True)
+    assert_gemm_close(y, ref, f"bf16 gelu M={M}")
 
 
 def test_gemm_bf16_modulation_shape():
