@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-graphs", action="store_true", help="skip the HIP-graph section")
     p.add_argument("--cpu-rows", type=int, default=12288)
     p.add_argument("--calib-copy", action="store_true")
     return p.parse_args()
@@ -235,6 +236,8 @@ def main():
                  "us": round(mod_us, 2),
                  "GBps_weight_read": round(6 * HIDDEN * HIDDEN * 2 / mod_us / 1e3, 1)}
 
+    graphs = None if args.no_graphs else graph_section(to_dev, ev, stream)
+
     # ----------------------------------------------------------- CPU oracle --
     cpu = None
     if not args.no_cpu:
@@ -256,10 +259,74 @@ def main():
         "roofline": roofline,
         "quantize": quant,
         "bf16_passthrough": bf16_pass,
+        "graphs": graphs,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(rec))
+
+
+def graph_section(to_dev, ev, stream):
+    """Launch overhead removed by HIP-graph capture: the launch-bound single
+    linear (X [128,1024], W [1024,1024], both quantized per call) and the
+    linear layers of one DiT block at 2048^2 with a CFG pair (33792 tokens)."""
+    import torch
+    import nvfp4_block_scaled_05_amd as nv
+    from nvfp4_block_scaled_05_amd import inputs
+    from nvfp4_block_scaled_05_amd.dit_block import DitBlockLinears, LAYERS, gemm_flops
+    from nvfp4_block_scaled_05_amd.graph import capture
+
+    def per_call_us(fn, iters):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters
+
+    d = inputs.linear_small()
+    x, w = to_dev(d["x"]), to_dev(d["w"])
+    qx = nv.quantize(x)
+    qw = nv.quantize(w)
+    y = nv.gemm(qx, qw)
+    ws_x = torch.empty(nv.quantize_workspace_bytes(*x.shape), dtype=torch.uint8, device=x.device)
+    ws_w = torch.empty(nv.quantize_workspace_bytes(*w.shape), dtype=torch.uint8, device=x.device)
+
+    def small():
+        nv.quantize(x, workspace=ws_x, out=(qx.codes, qx.scales, qx.tensor_scale))
+        nv.quantize(w, workspace=ws_w, out=(qw.codes, qw.scales, qw.tensor_scale))
+        nv.gemm(qx, qw, out=y, workspace=None)
+    small_eager = per_call_us(small, 200)
+    g_small = capture(small)
+    small_graph = per_call_us(g_small.replay, 200)
+
+    blk = inputs.dit_block_2048()
+    wts = {k: to_dev(blk[k]) for k in ("w_mod", "w_qkv", "w_o", "w_up", "w_down")}
+    acts = [to_dev(blk[k]) for k in ("temb", "x_qkv", "x_o", "x_mlp")]
+    del blk
+    block = DitBlockLinears(wts, tokens=acts[1].shape[0])
+    run = lambda: block(*acts)
+    block_eager = per_call_us(run, 5)
+    g_block = capture(run)
+    block_graph = per_call_us(g_block.replay, 5)
+    shapes = {"temb": tuple(acts[0].shape), "x_qkv": tuple(acts[1].shape),
+              "x_o": tuple(acts[2].shape), "x_mlp": tuple(acts[3].shape),
+              "h": (acts[3].shape[0], wts["w_up"].shape[0])}
+    shapes.update({k: tuple(v.shape) for k, v in wts.items()})
+    flops = gemm_flops(shapes)
+    total = sum(flops.values())
+    return {"linear_small_128x1024x1024": {"eager_us": round(small_eager, 2),
+                                           "graph_us": round(small_graph, 2)},
+            "dit_block_2048": {"layers": {k: ("nvfp4" if block.quantized[k] else "bf16")
+                                          for k in LAYERS},
+                               "tokens": acts[1].shape[0], "gflop": round(total / 1e9, 1),
+                               "eager_ms": round(block_eager / 1e3, 3),
+                               "graph_ms": round(block_graph / 1e3, 3),
+                               "graph_TFLOPs": round(total / (block_graph * 1e-6) / 1e12, 1)}}
 
 
 def cpu_baseline(data, rows):

@@ -17,8 +17,8 @@ from ._binding import EPILOGUES, Nvfp4Error, load
 Nvfp4Tensor = namedtuple("Nvfp4Tensor", ["codes", "scales", "tensor_scale", "cols"])
 
 __all__ = ["Nvfp4Tensor", "Nvfp4Error", "load", "abi_version", "status_string",
-           "quantize_workspace_bytes", "quantize", "dequantize", "gemm", "gemm_bf16",
-           "layer_is_quantized", "quantize_weight", "linear"]
+           "quantize_workspace_bytes", "quantize", "dequantize", "gemm", "gemm_workspace",
+           "gemm_bf16", "layer_is_quantized", "quantize_weight", "linear"]
 
 
 def _torch():
