@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 #define NVFP4_BLOCK 16 /* elements per block scale, [P1] "NVFP4量化" */
 
 typedef enum {
@@ -168,6 +168,34 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_t
                const void* bias_bf16, int64_t M, int64_t N, int64_t K, int epilogue,
                void* y_bf16, float* y_amax, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/*
+ * nvfp4_gemm_quantized -- the same GEMM with its output written in NVFP4
+ * under a static (calibrated) per-tensor scale ([P1] "NVFP4量化": the FP32
+ * tensor scale may be computed statically or dynamically), so the next
+ * layer's activation needs no bf16 round trip and no quantize pass.
+ *
+ * The bytes are exactly those of nvfp4_gemm (same inputs, bf16 Y) followed
+ * by nvfp4_quantize(Y, amax_in = y_amax): every output value is first rounded
+ * to bf16, then quantized in 16-element blocks along each row.
+ *
+ *   inputs, bias, M, N, K, epilogue  as nvfp4_gemm; additionally N % 16 == 0.
+ *   y_amax           device float, the static amax the tensor scale is
+ *                    derived from (s_enc = 2688 / amax, as in
+ *                    nvfp4_quantize); values above it saturate.  An Inf / NaN
+ *                    amax sets *y_tensor_scale to NaN and leaves the codes
+ *                    unspecified.
+ *   y_codes          out [M, N/2] bytes, 8-byte aligned.
+ *   y_scales         out [M, N/16] E4M3 bytes.
+ *   y_tensor_scale   out, 1 float (s_dec).
+ * Tiles are computed whole (no K split).
+ */
+int nvfp4_gemm_quantized(const uint8_t* a_codes, const uint8_t* a_scales,
+                         const float* a_tensor_scale, const uint8_t* w_codes,
+                         const uint8_t* w_scales, const float* w_tensor_scale,
+                         const void* bias_bf16, int64_t M, int64_t N, int64_t K, int epilogue,
+                         const float* y_amax, uint8_t* y_codes, uint8_t* y_scales,
+                         float* y_tensor_scale, void* stream);
 
 /*
  * nvfp4_gemm_workspace_bytes -- workspace bytes nvfp4_gemm can use for an

@@ -18,7 +18,7 @@ Nvfp4Tensor = namedtuple("Nvfp4Tensor", ["codes", "scales", "tensor_scale", "col
 
 __all__ = ["Nvfp4Tensor", "Nvfp4Error", "load", "abi_version", "status_string",
            "quantize_workspace_bytes", "quantize", "dequantize", "gemm", "gemm_workspace",
-           "gemm_bf16", "layer_is_quantized", "quantize_weight", "linear"]
+           "gemm_quantized", "gemm_bf16", "layer_is_quantized", "quantize_weight", "linear"]
 
 
 def _torch():
@@ -115,6 +115,28 @@ def gemm(a, w, bias=None, epilogue="none", y_amax=None, out=None, workspace=_NO_
                                      _ptr(y_amax), _ptr(workspace), ws_bytes, _stream()),
                    "nvfp4_gemm")
     return y
+
+
+def gemm_quantized(a, w, amax, bias=None, epilogue="none", out=None):
+    """The GEMM with NVFP4 output under the static amax ``amax`` (one-element
+    float32 device tensor): the same bytes as ``quantize(gemm(a, w), amax=amax)``.
+    Returns an ``Nvfp4Tensor``; ``out``: optional (codes, scales, tensor_scale)."""
+    torch = _torch()
+    M, N, K = a.codes.shape[0], w.codes.shape[0], a.cols
+    if w.cols != K:
+        raise ValueError("K mismatch")
+    dev = a.codes.device
+    if out is None:
+        out = (torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
+               torch.empty((M, N // 16), dtype=torch.uint8, device=dev),
+               torch.empty((1,), dtype=torch.float32, device=dev))
+    codes, scales, ts = out
+    _binding.check(load().nvfp4_gemm_quantized(_ptr(a.codes), _ptr(a.scales), _ptr(a.tensor_scale),
+                                               _ptr(w.codes), _ptr(w.scales), _ptr(w.tensor_scale),
+                                               _ptr(bias), M, N, K, EPILOGUES[epilogue], _ptr(amax),
+                                               _ptr(codes), _ptr(scales), _ptr(ts), _stream()),
+                   "nvfp4_gemm_quantized")
+    return Nvfp4Tensor(codes, scales, ts, N)
 
 
 def gemm_bf16(x, w, bias=None, epilogue="none", out=None):

@@ -31,6 +31,8 @@ SIGNATURES = {
     "nvfp4_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P,
                                   _P, ctypes.c_size_t, _P]),
     "nvfp4_gemm_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
+    "nvfp4_gemm_quantized": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
+                                            ctypes.c_int, _P, _P, _P, _P, _P]),
     "nvfp4_gemm_bf16": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
     "nvfp4_layer_is_quantized": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_char_p]),
 }

@@ -137,6 +137,32 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_t
                                              static_cast<hipStream_t>(stream)));
 }
 
+int nvfp4_gemm_quantized(const uint8_t* a_codes, const uint8_t* a_scales,
+                         const float* a_tensor_scale, const uint8_t* w_codes,
+                         const uint8_t* w_scales, const float* w_tensor_scale,
+                         const void* bias_bf16, int64_t M, int64_t N, int64_t K, int epilogue,
+                         const float* y_amax, uint8_t* y_codes, uint8_t* y_scales,
+                         float* y_tensor_scale, void* stream) {
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return NVFP4_ERR_SHAPE;
+  const bool empty = M == 0 || N == 0;
+  if (!empty && (!a_codes || !a_scales || !a_tensor_scale || !w_codes || !w_scales ||
+                 !w_tensor_scale || !y_amax || !y_codes || !y_scales || !y_tensor_scale))
+    return NVFP4_ERR_NULL;
+  if (K == 0 || K % 16 != 0 || N % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (((M + 127) / 128) * ((N + 127) / 128) >= ((int64_t)1 << 24)) return NVFP4_ERR_SHAPE;
+  if (!aligned(a_codes, 8) || !aligned(w_codes, 8) || !aligned(a_tensor_scale, 4) ||
+      !aligned(w_tensor_scale, 4) || !aligned(bias_bf16, 2) || !aligned(y_amax, 4) ||
+      !aligned(y_codes, 8) || !aligned(y_tensor_scale, 4))
+    return NVFP4_ERR_ALIGN;
+  if (epilogue != NVFP4_EPI_NONE && epilogue != NVFP4_EPI_GELU) return NVFP4_ERR_ARG;
+  int st = check_device();
+  if (st != NVFP4_OK) return st;
+  if (empty) return NVFP4_OK;
+  return hip_status(nvfp4::launch_gemm_nvfp4_quantized(
+      a_codes, a_scales, a_tensor_scale, w_codes, w_scales, w_tensor_scale, bias_bf16, M, N, K,
+      epilogue, y_amax, y_codes, y_scales, y_tensor_scale, static_cast<hipStream_t>(stream)));
+}
+
 int nvfp4_gemm_bf16(const void* x_bf16, const void* w_bf16, const void* bias_bf16, int64_t M,
                     int64_t N, int64_t K, int epilogue, void* y_bf16, void* stream) {
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return NVFP4_ERR_SHAPE;

@@ -148,4 +148,61 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+
+// ------------------------------------------------------------- quantizer --
+// Shared by the quantize kernel and the GEMM epilogue that writes NVFP4
+// output, so both produce the same bytes for the same bf16 values.
+
+// Largest |x| of 8 bf16 values (one 16-byte word), as two 16-bit magnitudes.
+__device__ __forceinline__ u16x2 max8(u32x4 a) {
+  return max_u16x2(max_u16x2(abs_halves(a.x), abs_halves(a.y)),
+                   max_u16x2(abs_halves(a.z), abs_halves(a.w)));
+}
+
+// Per-tensor scales from the tensor amax (a finite binary32): s_enc = 2688 /
+// amax and s_dec = 1 / s_enc, both correctly rounded; below 2^-96 the tensor
+// is degenerate (s_enc = s_dec = 1, every block scale 0).
+__device__ __forceinline__ void tensor_scales(float amax, bool& degenerate, float& s_enc,
+                                              float& s_dec) {
+  degenerate = amax < 0x1p-96f;
+  s_enc = degenerate ? 1.0f : 2688.0f / amax;
+  s_dec = degenerate ? 1.0f : 1.0f / s_enc;
+}
+
+// E2M1 codes of 8 bf16 values (one 16-byte word) times e, packed.
+__device__ __forceinline__ uint32_t encode8(u32x4 v, float e) {
+  uint32_t c = 0;
+  c = e2m1_pack2<0>(c, bf16_bits_to_f32(v.x & 0xFFFFu) * e, bf16_bits_to_f32(v.x >> 16) * e);
+  c = e2m1_pack2<1>(c, bf16_bits_to_f32(v.y & 0xFFFFu) * e, bf16_bits_to_f32(v.y >> 16) * e);
+  c = e2m1_pack2<2>(c, bf16_bits_to_f32(v.z & 0xFFFFu) * e, bf16_bits_to_f32(v.z >> 16) * e);
+  c = e2m1_pack2<3>(c, bf16_bits_to_f32(v.w & 0xFFFFu) * e, bf16_bits_to_f32(v.w >> 16) * e);
+  return c;
+}
+
+// Sign-only codes (block scale 0): nibble = 8 for a negative input, else 0.
+__device__ __forceinline__ uint32_t signs8(u32x4 v) {
+  uint32_t c = 0;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c |= ((w[j] >> 15) & 1u) << (8 * j + 3);
+    c |= ((w[j] >> 31) & 1u) << (8 * j + 7);
+  }
+  return c;
+}
+
+// One 16-element block: scale byte and 8 bytes of codes.
+__device__ __forceinline__ void quantize_block(u32x4 lo, u32x4 hi, bool degenerate, float s_enc,
+                                               float s_dec, u32x2& c, uint32_t& S) {
+  const u16x2 m = max_u16x2(max8(lo), max8(hi));
+  const float a_b = bf16_bits_to_f32(m.x > m.y ? m.x : m.y);
+  S = degenerate ? 0u : e4m3_from_f32_rne((a_b / 6.0f) * s_enc);
+  if (S == 0) {
+    c = u32x2{signs8(lo), signs8(hi)};
+  } else {
+    const float e = 1.0f / (e4m3_to_f32(S) * s_dec);
+    c = u32x2{encode8(lo, e), encode8(hi, e)};
+  }
+}
+
 }  // namespace nvfp4

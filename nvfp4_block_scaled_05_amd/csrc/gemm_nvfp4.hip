@@ -313,6 +313,98 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::TM][C::TN], floa
   }
 }
 
+// Where a tile's results go: bf16 Y (with an optional amax), or -- when
+// `codes` is set -- Y quantized to NVFP4 with the static tensor scale derived
+// from *amax_static, the same bytes as quantizing the bf16 Y with that amax.
+struct Out {
+  uint16_t* y;
+  uint32_t* y_amax;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* tensor_scale;
+  const float* amax_static;
+};
+
+// NVFP4 output.  The tile's bf16 values (computed exactly as in epilogue())
+// are staged row-major in LDS half a tile at a time; then each thread takes
+// whole 16-element blocks of a row through quantize_block(), the quantizer's
+// own routine.  Needs N % 16 == 0 and (BM/2) * (BN+8) halves of LDS.
+template <class C>
+__device__ __forceinline__ void epilogue_quant(const f32x16 (&acc)[C::TM][C::TN], float scale,
+                                               const uint16_t* __restrict__ bias, int epi,
+                                               int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                               const Out& out, uint8_t* lds) {
+  constexpr int kHalf = C::BM / 2;
+  constexpr int kPitch = C::BN + 8;      // halves per staged row (spreads the banks)
+  constexpr int kBlocks = C::BN / 16;    // 16-blocks per staged row
+  static_assert(kHalf % C::WM == 0, "each wave's rows lie in one half of the tile");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds);
+  // tensor scales as the quantizer derives them from a given amax
+  const uint32_t amax_bits = __float_as_uint(*out.amax_static) & 0x7FFFFFFFu;
+  if (amax_bits >= 0x7F800000u) {                  // Inf / NaN amax: no scale exists
+    if (blockIdx.x == 0 && threadIdx.x == 0) *out.tensor_scale = __uint_as_float(0x7FC00000u);
+    return;
+  }
+  bool degenerate;
+  float s_enc, s_dec;
+  tensor_scales(__uint_as_float(amax_bits), degenerate, s_enc, s_dec);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *out.tensor_scale = s_dec;
+  const int64_t code_pitch = N / 2, scale_pitch = N / 16;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((wm * C::WM) / kHalf == half) {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int cl = wn * C::WN + j * 32 + (lane & 31);
+        const int64_t col = n0 + cl;
+        const float bv = (bias && col < N) ? bf16_bits_to_f32(bias[col]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            const int rl = wm * C::WM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3) - half * kHalf;
+            float v0 = __builtin_fmaf(acc[i][j][e], scale, bv);
+            float v1 = __builtin_fmaf(acc[i][j][e + 1], scale, bv);
+            if (epi == 1) {
+              v0 = gelu_erf(v0);
+              v1 = gelu_erf(v1);
+            }
+            const uint32_t pk = bf16x2_rne(v0, v1);
+            stage[rl * kPitch + cl] = (uint16_t)pk;
+            stage[(rl + 1) * kPitch + cl] = (uint16_t)(pk >> 16);
+          }
+      }
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < kHalf * kBlocks; b += C::NT) {
+      const int rl = b / kBlocks, cb = b % kBlocks;
+      const int64_t row = m0 + half * kHalf + rl, col = n0 + cb * 16;
+      if (row < M && col < N) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(stage + rl * kPitch + cb * 16);
+        u32x2 c;
+        uint32_t S;
+        quantize_block(src[0], src[1], degenerate, s_enc, s_dec, c, S);
+        *reinterpret_cast<u32x2*>(out.codes + row * code_pitch + col / 2) = c;
+        out.scales[row * scale_pitch + col / 16] = (uint8_t)S;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void finish_tile(const f32x16 (&acc)[C::TM][C::TN], float scale,
+                                            const uint16_t* __restrict__ bias, int epi, int64_t M,
+                                            int64_t N, int64_t m0, int64_t n0, const Out& out,
+                                            uint8_t* lds) {
+  if (out.codes)
+    epilogue_quant<C>(acc, scale, bias, epi, M, N, m0, n0, out, lds);
+  else
+    epilogue<C>(acc, scale, bias, epi, M, N, m0, n0, out.y, out.y_amax);
+}
+
 // Position, in XCD-contiguous order, of workgroup b among the first T
 // workgroups: they are dealt to the XCDs round-robin, so the ones on XCD k
 // (b % 8 == k) take the k-th contiguous range of positions.
@@ -348,11 +440,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ sa, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ sw,
-    const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi,
-    uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax, int vec_flags) {
+    const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi, Out out,
+    int vec_flags) {
   using T = C;
   constexpr int BM = C::BM, BN = C::BN;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * T::STAGE];
+  static_assert(BM / 2 * (BN + 8) * 2 <= 2 * T::STAGE, "LDS for the NVFP4 epilogue");
 
   const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int64_t tm, tn;
@@ -373,7 +466,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_kernel(
   else
     main_loop<C, true>(A, Wt, m0, n0, K, vec16, vec8, lds, acc);
 
-  epilogue<C>(acc, (*sa) * (*sw), bias, epi, M, N, m0, n0, y, y_amax);
+  finish_tile<C>(acc, (*sa) * (*sw), bias, epi, M, N, m0, n0, out, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -690,10 +783,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_pipe_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ sa, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ sw,
-    const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi,
-    uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax, int vec_flags, SplitK sk) {
+    const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi, Out out,
+    int vec_flags, SplitK sk) {
   using L = Lay2<C>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::STAGE];
+  static_assert(C::BM / 2 * (C::BN + 8) * 2 <= 2 * L::STAGE, "LDS for the NVFP4 epilogue");
   const int64_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
   int64_t tm, tn, tail;
   int split;
@@ -717,7 +811,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_pipe_kernel(
     store_partial<C>(acc, sk, tail, split);
     return;
   }
-  epilogue<C>(acc, (*sa) * (*sw), bias, epi, M, N, m0, n0, y, y_amax);
+  finish_tile<C>(acc, (*sa) * (*sw), bias, epi, M, N, m0, n0, out, lds);
 }
 
 __global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
@@ -725,8 +819,8 @@ __global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
 template <class C>
 hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const float* sa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* sw,
-                       const void* bias, int64_t M, int64_t N, int64_t K, int epi, void* y,
-                       uint32_t* amax, hipStream_t stream) {
+                       const void* bias, int64_t M, int64_t N, int64_t K, int epi,
+                       const Out& out, hipStream_t stream) {
   const int64_t tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
   const uintptr_t align_bits = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(w_codes);
   const bool vec16 = (K % 32 == 0) && (align_bits & 15) == 0;
@@ -734,8 +828,8 @@ hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   const bool vec8 = ((K / 16) % 8 == 0) && (salign & 7) == 0;
   hipLaunchKernelGGL((gemm_nvfp4_kernel<C>), dim3((unsigned)tiles), dim3(C::NT), 0, stream,
                      a_codes, a_scales, sa, w_codes, w_scales, sw,
-                     reinterpret_cast<const uint16_t*>(bias), M, N, K, epi,
-                     reinterpret_cast<uint16_t*>(y), amax, (vec16 ? 1 : 0) | (vec8 ? 2 : 0));
+                     reinterpret_cast<const uint16_t*>(bias), M, N, K, epi, out,
+                     (vec16 ? 1 : 0) | (vec8 ? 2 : 0));
   return hipGetLastError();
 }
 
@@ -796,8 +890,8 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_pipe(const uint8_t* a_codes, const uint8_t* a_scales, const float* sa,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* sw,
-                       const void* bias, int64_t M, int64_t N, int64_t K, int epi, void* y,
-                       uint32_t* amax, void* workspace, size_t workspace_bytes,
+                       const void* bias, int64_t M, int64_t N, int64_t K, int epi,
+                       const Out& out, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
   using C = CfgPipe;
   const uintptr_t cal = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(w_codes);
@@ -805,20 +899,21 @@ hipError_t launch_pipe(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   // interior fast path: 16-byte code rows, 4-byte scale rows
   const bool vec = (K % 64 == 0) && (cal & 15) == 0 && (sal & 3) == 0;
   const SplitPlan plan = plan_split(M, N, K);
-  const bool split = plan.ways > 1 && workspace && workspace_bytes >= plan.bytes;
+  // (NVFP4 output is written by whole tiles only)
+  const bool split = plan.ways > 1 && workspace && workspace_bytes >= plan.bytes && !out.codes;
   const SplitK sk = split ? SplitK{static_cast<float*>(workspace), plan.main_tiles, plan.ways}
                           : SplitK{nullptr, plan.tiles, 1};
   const int64_t grid = split ? plan.main_tiles + plan.tail * plan.ways : plan.tiles;
   hipLaunchKernelGGL((gemm_nvfp4_pipe_kernel<C>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
                      a_codes, a_scales, sa, w_codes, w_scales, sw,
-                     reinterpret_cast<const uint16_t*>(bias), M, N, K, epi,
-                     reinterpret_cast<uint16_t*>(y), amax, vec ? 4 : 0, sk);
+                     reinterpret_cast<const uint16_t*>(bias), M, N, K, epi, out, vec ? 4 : 0,
+                     sk);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   hipLaunchKernelGGL((split_reduce_kernel<C>), dim3((unsigned)(plan.tail * (C::BM / kReduceRows))),
                      dim3(256), 0, stream, static_cast<const float*>(workspace), plan.main_tiles,
-                     plan.ways, sa, sw, reinterpret_cast<const uint16_t*>(bias), M, N, epi,
-                     reinterpret_cast<uint16_t*>(y), amax);
+                     plan.ways, sa, sw, reinterpret_cast<const uint16_t*>(bias), M, N, epi, out.y,
+                     out.y_amax);
   return hipGetLastError();
 }
 
@@ -829,24 +924,50 @@ size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return plan_split(M, N, K).bytes;
 }
 
+namespace {
+
+hipError_t launch_any(const uint8_t* a_codes, const uint8_t* a_scales, const float* sa,
+                      const uint8_t* w_codes, const uint8_t* w_scales, const float* sw,
+                      const void* bias, int64_t M, int64_t N, int64_t K, int epilogue,
+                      const Out& out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (out.y_amax) {
+    hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, stream, out.y_amax);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (M == 0 || N == 0) return hipSuccess;
+  if (use_pipe(M, N))
+    return launch_pipe(a_codes, a_scales, sa, w_codes, w_scales, sw, bias, M, N, K, epilogue, out,
+                       workspace, workspace_bytes, stream);
+  return launch_tile<CfgSmall>(a_codes, a_scales, sa, w_codes, w_scales, sw, bias, M, N, K,
+                               epilogue, out, stream);
+}
+
+}  // namespace
+
 hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales,
                              const float* a_tensor_scale, const uint8_t* w_codes,
                              const uint8_t* w_scales, const float* w_tensor_scale,
                              const void* bias, int64_t M, int64_t N, int64_t K, int epilogue,
                              void* y, float* y_amax, void* workspace, size_t workspace_bytes,
                              hipStream_t stream) {
-  uint32_t* amax = reinterpret_cast<uint32_t*>(y_amax);
-  if (amax) {
-    hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, stream, amax);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (M == 0 || N == 0) return hipSuccess;
-  if (use_pipe(M, N))
-    return launch_pipe(a_codes, a_scales, a_tensor_scale, w_codes, w_scales, w_tensor_scale, bias, M,
-                       N, K, epilogue, y, amax, workspace, workspace_bytes, stream);
-  return launch_tile<CfgSmall>(a_codes, a_scales, a_tensor_scale, w_codes, w_scales,
-                               w_tensor_scale, bias, M, N, K, epilogue, y, amax, stream);
+  const Out out{reinterpret_cast<uint16_t*>(y), reinterpret_cast<uint32_t*>(y_amax), nullptr,
+                nullptr, nullptr, nullptr};
+  return launch_any(a_codes, a_scales, a_tensor_scale, w_codes, w_scales, w_tensor_scale, bias, M,
+                    N, K, epilogue, out, workspace, workspace_bytes, stream);
+}
+
+hipError_t launch_gemm_nvfp4_quantized(const uint8_t* a_codes, const uint8_t* a_scales,
+                                       const float* a_tensor_scale, const uint8_t* w_codes,
+                                       const uint8_t* w_scales, const float* w_tensor_scale,
+                                       const void* bias, int64_t M, int64_t N, int64_t K,
+                                       int epilogue, const float* y_amax_static, uint8_t* y_codes,
+                                       uint8_t* y_scales, float* y_tensor_scale,
+                                       hipStream_t stream) {
+  const Out out{nullptr, nullptr, y_codes, y_scales, y_tensor_scale, y_amax_static};
+  return launch_any(a_codes, a_scales, a_tensor_scale, w_codes, w_scales, w_tensor_scale, bias, M,
+                    N, K, epilogue, out, nullptr, 0, stream);
 }
 
 }  // namespace nvfp4

@@ -26,6 +26,16 @@ hipError_t launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales,
                              void* y, float* y_amax, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+// The same GEMM writing Y as NVFP4 (codes, scales, tensor scale) quantized
+// with the static amax *y_amax_static; N % 16 == 0.
+hipError_t launch_gemm_nvfp4_quantized(const uint8_t* a_codes, const uint8_t* a_scales,
+                                       const float* a_tensor_scale, const uint8_t* w_codes,
+                                       const uint8_t* w_scales, const float* w_tensor_scale,
+                                       const void* bias, int64_t M, int64_t N, int64_t K,
+                                       int epilogue, const float* y_amax_static, uint8_t* y_codes,
+                                       uint8_t* y_scales, float* y_tensor_scale,
+                                       hipStream_t stream);
+
 // Workspace bytes launch_gemm_nvfp4 can use to split the tail tiles over K
 // (0: no split for this shape).
 size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);

@@ -31,11 +31,6 @@ namespace nvfp4 {
 
 static constexpr int kQuantThreads = 256;
 
-__device__ __forceinline__ u16x2 max8(u32x4 a) {
-  return max_u16x2(max_u16x2(abs_halves(a.x), abs_halves(a.y)),
-                   max_u16x2(abs_halves(a.z), abs_halves(a.w)));
-}
-
 // Partial amax: workgroup b scans its contiguous chunk of 16-byte words, U
 // loads in flight per thread, and writes max |x| of the chunk.
 template <int U>
@@ -83,42 +78,6 @@ __device__ __forceinline__ uint32_t fold_amax_words(const uint32_t* __restrict__
   return r;
 }
 
-// E2M1 codes of 8 bf16 values (one 16-byte word) times e, packed.
-__device__ __forceinline__ uint32_t encode8(u32x4 v, float e) {
-  uint32_t c = 0;
-  c = e2m1_pack2<0>(c, bf16_bits_to_f32(v.x & 0xFFFFu) * e, bf16_bits_to_f32(v.x >> 16) * e);
-  c = e2m1_pack2<1>(c, bf16_bits_to_f32(v.y & 0xFFFFu) * e, bf16_bits_to_f32(v.y >> 16) * e);
-  c = e2m1_pack2<2>(c, bf16_bits_to_f32(v.z & 0xFFFFu) * e, bf16_bits_to_f32(v.z >> 16) * e);
-  c = e2m1_pack2<3>(c, bf16_bits_to_f32(v.w & 0xFFFFu) * e, bf16_bits_to_f32(v.w >> 16) * e);
-  return c;
-}
-
-// Sign-only codes (block scale 0): nibble = 8 for a negative input, else 0.
-__device__ __forceinline__ uint32_t signs8(u32x4 v) {
-  uint32_t c = 0;
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    c |= ((w[j] >> 15) & 1u) << (8 * j + 3);
-    c |= ((w[j] >> 31) & 1u) << (8 * j + 7);
-  }
-  return c;
-}
-
-// One 16-element block: scale byte and 8 bytes of codes.
-__device__ __forceinline__ void quantize_block(u32x4 lo, u32x4 hi, bool degenerate, float s_enc,
-                                               float s_dec, u32x2& c, uint32_t& S) {
-  const u16x2 m = max_u16x2(max8(lo), max8(hi));
-  const float a_b = bf16_bits_to_f32(m.x > m.y ? m.x : m.y);
-  S = degenerate ? 0u : e4m3_from_f32_rne((a_b / 6.0f) * s_enc);
-  if (S == 0) {
-    c = u32x2{signs8(lo), signs8(hi)};
-  } else {
-    const float e = 1.0f / (e4m3_to_f32(S) * s_dec);
-    c = u32x2{encode8(lo, e), encode8(hi, e)};
-  }
-}
-
 // Every workgroup folds the amax words, derives s_enc / s_dec, then each
 // thread quantizes U blocks per round (all 2U loads issued first).
 template <int U>
@@ -135,10 +94,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
     }
     return;
   }
-  const float amax = __uint_as_float(amax_bits);
-  const bool degenerate = amax < 0x1p-96f;
-  const float s_enc = degenerate ? 1.0f : 2688.0f / amax;
-  const float s_dec = degenerate ? 1.0f : 1.0f / s_enc;
+  bool degenerate;
+  float s_enc, s_dec;
+  tensor_scales(__uint_as_float(amax_bits), degenerate, s_enc, s_dec);
   if (first) {
     *tensor_scale = s_dec;
     if (dev_status) *dev_status = 0;

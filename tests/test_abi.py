@@ -34,14 +34,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(lib, n), n
         assert n in _binding.SIGNATURES, n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.nvfp4_abi_version() == 2
+    assert lib.nvfp4_abi_version() == 3
     for code in range(-8, 1):
         assert lib.nvfp4_status_string(code)
     assert lib.nvfp4_status_string(-99) == b"unknown status"
@@ -127,6 +127,19 @@ def test_gemm_argument_errors(lib):
     assert b(A, A, None, 8, 8, 12, 0, A, None) == SHAPE
     assert b(A + 8, A, None, 8, 8, 64, 0, A, None) == ALIGN
     assert b(A, A, None, 8, 8, 64, 3, A, None) == ARG
+
+
+def test_gemm_quantized_argument_errors(lib):
+    def gq(M=64, N=64, K=64, amax=A, yc=A, ys=A, yt=A, epi=0):
+        return lib.nvfp4_gemm_quantized(A, A, A, A, A, A, None, M, N, K, epi, amax, yc, ys, yt, None)
+    assert gq(amax=None) == NULL
+    assert gq(yc=None) == NULL
+    assert gq(N=40) == SHAPE            # output blocks of 16 along N
+    assert gq(K=24) == SHAPE
+    assert gq(yc=A + 4) == ALIGN
+    assert gq(yt=A + 2) == ALIGN
+    assert gq(epi=5) == ARG
+    assert gq(M=0, amax=None, yc=None, ys=None, yt=None) in (OK, DEVICE)
 
 
 def test_layer_predicate_matches_python_re(lib):

@@ -373,6 +373,69 @@ def test_gemm_k_split_deterministic_with_amax(monkeypatch):
     assert float((ulp_diff(y1, whole) > 1).mean()) <= 1e-3   # only the fp32 addition order differs
 
 
+# ------------------------------------------------ NVFP4 output, static scale --
+
+def _gemm_quantized_case(M, N, K, seed, amax_factor, epilogue="none", bias=False):
+    import torch
+    a_bits = W.random_matrix(seed, (M, K), "t3")
+    w_bits = W.random_matrix(seed + 1, (N, K), "normal", 0.02)
+    b = to_dev(W.random_matrix(seed + 2, (1, N), "normal", 0.1)[0]) if bias else None
+    qa, qw = gpu_quantize(a_bits), gpu_quantize(w_bits)
+    amax = torch.empty((1,), dtype=torch.float32, device="cuda")
+    y = nv.gemm(qa, qw, bias=b, epilogue=epilogue, y_amax=amax)
+    static = amax * amax_factor                       # a calibrated amax, above or below the true one
+    fused = nv.gemm_quantized(qa, qw, static, bias=b, epilogue=epilogue)
+    two_step = nv.quantize(y, amax=static)
+    _sync()
+    return y, static, fused, two_step
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 528, 1088), (257, 16, 64), (64, 1024, 2048)])
+@pytest.mark.parametrize("kernel", ["small", "pipe"])
+def test_gemm_quantized_equals_gemm_then_quantize(monkeypatch, M, N, K, kernel):
+    monkeypatch.setenv("NVFP4_GEMM_KERNEL", kernel)
+    for factor, epi, bias in ((1.0, "gelu", True), (0.25, "none", False), (8.0, "none", True)):
+        y, static, fused, two = _gemm_quantized_case(M, N, K, M + N + K, factor, epi, bias)
+        for u, v, what in ((fused.codes, two.codes, "codes"), (fused.scales, two.scales, "scales"),
+                           (fused.tensor_scale, two.tensor_scale, "tensor scale")):
+            assert torch_equal(u, v), f"{kernel} {M}x{N}x{K} amax*{factor}: {what}"
+        # and the quantizer half against the oracle, on the GPU's bf16 output
+        ref = o_quantize(bits_of(y), amax=np.float32(static.item()))
+        assert_quant_equal(fused, ref, f"oracle {kernel} amax*{factor}")
+        if factor < 1.0:
+            assert (ref.scales == 0x7E).any()     # the static scale saturates some blocks
+
+
+def torch_equal(u, v):
+    import torch
+    return bool(torch.equal(u, v))
+
+
+def test_gemm_quantized_mlp_up_full_size():
+    # H of the MLP at 2048^2 written straight in NVFP4 under a static amax
+    import torch
+    x_bits = _mlp()["x"]
+    wu_bits, _ = _oracle_weight("w_up")
+    qx, qwu = gpu_quantize(x_bits), gpu_quantize(wu_bits)
+    amax = torch.empty((1,), dtype=torch.float32, device="cuda")
+    h = nv.gemm(qx, qwu, epilogue="gelu", y_amax=amax)
+    static = amax * 0.75
+    fused = nv.gemm_quantized(qx, qwu, static, epilogue="gelu")
+    two = nv.quantize(h, amax=static)
+    _sync()
+    assert torch_equal(fused.codes, two.codes) and torch_equal(fused.scales, two.scales)
+    assert torch_equal(fused.tensor_scale, two.tensor_scale)
+
+
+def test_gemm_quantized_nonfinite_amax():
+    import torch
+    qa = gpu_quantize(W.random_matrix(5, (64, 64)))
+    qw = gpu_quantize(W.random_matrix(6, (32, 64), "normal", 0.02))
+    fused = nv.gemm_quantized(qa, qw, torch.full((1,), float("inf"), device="cuda"))
+    _sync()
+    assert np.isnan(fused.tensor_scale.item())
+
+
 # ------------------------------------------------------- bf16 passthrough --
 
 @pytest.mark.parametrize("M,N,K", [(64, 64, 64), (130, 70, 40), (2, 1000, 3072), (300, 257, 1024),
