@@ -19,12 +19,6 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// 128-bit load marked non-temporal (last use of the data: stream it through).
-__device__ __forceinline__ uint4 load_nt(const uint4* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // Largest |x| of the two bf16 halves of a word, as a 16-bit magnitude pattern.
 __device__ __forceinline__ u16x2 abs_halves(uint32_t w) {
   return __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);

@@ -24,7 +24,7 @@ static constexpr int TILE_ELEMS = BM * PITCH;
 // bf16 operand [rows, K], K % 8 == 0.  Per K step: 128 rows x 8 chunks of
 // 8 bf16 = 1024 chunks; 4 per thread.
 struct Bf16Tile {
-  uint4 v[4];
+  u32x4 v[4];
 };
 
 __device__ __forceinline__ void load_bf16(const uint16_t* __restrict__ x, int64_t rows, int64_t K,
@@ -35,9 +35,9 @@ __device__ __forceinline__ void load_bf16(const uint16_t* __restrict__ x, int64_
     const int64_t row = row0 + (q >> 3);
     const int64_t k = k0 + (q & 7) * 8;
     if (row < rows && k < K)
-      t.v[i] = *reinterpret_cast<const uint4*>(x + row * K + k);
+      t.v[i] = *reinterpret_cast<const u32x4*>(x + row * K + k);
     else
-      t.v[i] = make_uint4(0u, 0u, 0u, 0u);
+      t.v[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -45,7 +45,7 @@ __device__ __forceinline__ void store_bf16(const Bf16Tile& t, uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = threadIdx.x + i * NT;
-    *reinterpret_cast<uint4*>(lds + (q >> 3) * PITCH + (q & 7) * 8) = t.v[i];
+    *reinterpret_cast<u32x4*>(lds + (q >> 3) * PITCH + (q & 7) * 8) = t.v[i];
   }
 }
 
@@ -60,13 +60,13 @@ __device__ __forceinline__ void mma_step(const uint16_t* __restrict__ As,
   const int r = lane & 31, kh = (lane >> 5) * 8;
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) {
-    uint4 a[2], b[2];
+    u32x4 a[2], b[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      a[i] = *reinterpret_cast<const uint4*>(As + (wm * 64 + i * 32 + r) * PITCH + kk * 16 + kh);
+      a[i] = *reinterpret_cast<const u32x4*>(As + (wm * 64 + i * 32 + r) * PITCH + kk * 16 + kh);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const uint4*>(Bs + (wn * 64 + j * 32 + r) * PITCH + kk * 16 + kh);
+      b[j] = *reinterpret_cast<const u32x4*>(Bs + (wn * 64 + j * 32 + r) * PITCH + kk * 16 + kh);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll

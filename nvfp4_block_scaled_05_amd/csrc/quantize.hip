@@ -128,33 +128,29 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
   }
 }
 
-// Dequantize: y = bf16_rne((value * S) * s_dec); one thread per 16-block.
+// Dequantize: y = bf16_rne((value * S) * s_dec); one thread per 16-block per
+// round: one 8-byte code load, one scale byte, two streaming 16-byte stores.
+// The products are binary32 (the first is exact); the packed conversion
+// rounds to nearest-even.
 __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
-    const uint2* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ tensor_scale, int64_t nblocks, uint4* __restrict__ y) {
+    const u32x2* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const float* __restrict__ tensor_scale, int64_t nblocks, u32x4* __restrict__ y) {
   const float s_dec = *tensor_scale;
   const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
   for (int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; b < nblocks; b += stride) {
-    const uint2 c = codes[b];
+    const u32x2 c = __builtin_nontemporal_load(codes + b);
     const float S = e4m3_to_f32(scales[b]);
     uint32_t out[8];
-    const uint32_t w[2] = {c.x, c.y};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      f32x2 p0 = e2m1_unpack2_f32<0>(w[h]);
-      f32x2 p1 = e2m1_unpack2_f32<1>(w[h]);
-      f32x2 p2 = e2m1_unpack2_f32<2>(w[h]);
-      f32x2 p3 = e2m1_unpack2_f32<3>(w[h]);
-      const f32x2 p[4] = {p0, p1, p2, p3};
+      const uint32_t w = h ? c.y : c.x;
+      const f32x2 p[4] = {e2m1_unpack2_f32<0>(w), e2m1_unpack2_f32<1>(w), e2m1_unpack2_f32<2>(w),
+                          e2m1_unpack2_f32<3>(w)};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float y0 = (p[j].x * S) * s_dec;
-        const float y1 = (p[j].y * S) * s_dec;
-        out[4 * h + j] = bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16);
-      }
+      for (int j = 0; j < 4; ++j) out[4 * h + j] = bf16x2_rne((p[j].x * S) * s_dec, (p[j].y * S) * s_dec);
     }
-    y[2 * b] = make_uint4(out[0], out[1], out[2], out[3]);
-    y[2 * b + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+    __builtin_nontemporal_store(u32x4{out[0], out[1], out[2], out[3]}, y + 2 * b);
+    __builtin_nontemporal_store(u32x4{out[4], out[5], out[6], out[7]}, y + 2 * b + 1);
   }
 }
 
@@ -242,8 +238,8 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
   const int64_t nblocks = rows * cols / 16;
   const int g = grid_for(nblocks, 4, 8192);
   hipLaunchKernelGGL(dequantize_kernel, dim3(g), dim3(kQuantThreads), 0, stream,
-                     reinterpret_cast<const uint2*>(codes), scales, tensor_scale, nblocks,
-                     reinterpret_cast<uint4*>(y));
+                     reinterpret_cast<const u32x2*>(codes), scales, tensor_scale, nblocks,
+                     reinterpret_cast<u32x4*>(y));
   return hipGetLastError();
 }
 
