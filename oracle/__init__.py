@@ -37,6 +37,8 @@ Module map:
   gemm.py    -- block-scaled GEMM (exact integer form and fp64 form), GELU,
                 bf16 passthrough linear.
   layers.py  -- the exclude-pattern layer predicate.
+  fp8.py     -- the FP8 row-wise variant ("fp8r"): quantize, dequantize, W8A8
+                GEMM (reading R-22: the pages name the variant, not its recipe).
 """
 
 from .formats import (E2M1_MAGNITUDES, e2m1_encode_magnitude, e2m1_value,
@@ -46,6 +48,8 @@ from .quant import NonFiniteInput, Quantized, quantize, dequantize, unpack_codes
 from .gemm import (block_values_f64, gemm_fp64, gemm_exact_rows, gelu_f64,
                    epilogue_to_bf16, linear_bf16_fp64)
 from .layers import EXCLUDE_PATTERN, layer_is_quantized
+from .fp8 import (Fp8Rowwise, quantize_fp8_rowwise, dequantize_fp8_rowwise,
+                  gemm_fp8_exact_rows, gemm_fp8_fp64)
 
 __all__ = [
     "E2M1_MAGNITUDES", "e2m1_encode_magnitude", "e2m1_value",
@@ -55,4 +59,6 @@ __all__ = [
     "block_values_f64", "gemm_fp64", "gemm_exact_rows", "gelu_f64",
     "epilogue_to_bf16", "linear_bf16_fp64",
     "EXCLUDE_PATTERN", "layer_is_quantized",
+    "Fp8Rowwise", "quantize_fp8_rowwise", "dequantize_fp8_rowwise",
+    "gemm_fp8_exact_rows", "gemm_fp8_fp64",
 ]
