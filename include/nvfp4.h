@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 3
+#define NVFP4_ABI_VERSION 4
 #define NVFP4_BLOCK 16 /* elements per block scale, [P1] "NVFP4量化" */
 
 typedef enum {
@@ -203,6 +203,42 @@ int nvfp4_gemm_quantized(const uint8_t* a_codes, const uint8_t* a_scales,
  * only; at most 256 KiB per compute unit (64 MiB on a 256-CU device).
  */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * The FP8 row-wise variant ("fp8r").  [P3] selects FP8 as the other quantized
+ * variant of the model (the paragraph on run options) and gives no recipe;
+ * here it is FP8 with row-wise scales: one FP32 scale per row of the
+ * activation (per token, dynamic on every call) and per row of the weight
+ * (per output channel, when the weights are loaded), E4M3 elements (sign in
+ * bit 7), and a GEMM on the native FP8 matrix cores with the two row scales
+ * applied in the epilogue.
+ *
+ * nvfp4_fp8_quantize_rowwise -- per row r of x [rows, cols]:
+ *   amax_r = max|x|;  s_r = 448 / amax_r;  d_r = 1 / s_r  (binary32, RNE);
+ *   amax_r < 2^-96: s_r = d_r = 1;
+ *   codes[r, k] = sign(x) << 7 | E4M3(|x| * s_r), nearest-even, saturating.
+ *   x_bf16      [rows, cols] bf16, 16-byte aligned; cols > 0, cols % 16 == 0.
+ *   codes       out [rows, cols] E4M3 bytes, 8-byte aligned.
+ *   row_scales  out [rows] float: d_r.
+ *   dev_status  optional device int32: NVFP4_OK, or NVFP4_ERR_NONFINITE if a
+ *               row holds Inf / NaN (that row's scale is NaN, its codes
+ *               unspecified).
+ */
+int nvfp4_fp8_quantize_rowwise(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes,
+                               float* row_scales, int32_t* dev_status, void* stream);
+
+/*
+ * nvfp4_fp8_gemm -- Y[m,n] = bf16_rne( epi( (sum_k value(A[m,k]) * value(W[n,k]))
+ *                                            * (a_scales[m] * w_scales[n]) + bias[n] ) ),
+ * fp32 accumulation of the exact E4M3 products, the scale product in binary32.
+ *   a_codes / a_scales  [M, K] / [M] from nvfp4_fp8_quantize_rowwise;
+ *   w_codes / w_scales  [N, K] / [N];  code pointers 16-byte aligned.
+ *   bias_bf16 optional [N];  M, N >= 0, K > 0, K % 16 == 0.
+ *   y_bf16 out [M, N] bf16, 2-byte aligned.
+ */
+int nvfp4_fp8_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_codes,
+                   const float* w_scales, const void* bias_bf16, int64_t M, int64_t N, int64_t K,
+                   int epilogue, void* y_bf16, void* stream);
 
 /*
  * nvfp4_gemm_bf16 -- the bf16 passthrough for layers kept in higher precision

@@ -15,10 +15,11 @@ from . import _binding
 from ._binding import EPILOGUES, Nvfp4Error, load
 
 Nvfp4Tensor = namedtuple("Nvfp4Tensor", ["codes", "scales", "tensor_scale", "cols"])
+Fp8Tensor = namedtuple("Fp8Tensor", ["codes", "scales"])   # E4M3 [rows, cols], float [rows]
 
-__all__ = ["Nvfp4Tensor", "Nvfp4Error", "load", "abi_version", "status_string",
+__all__ = ["Nvfp4Tensor", "Fp8Tensor", "Nvfp4Error", "load", "abi_version", "status_string",
            "quantize_workspace_bytes", "quantize", "dequantize", "gemm", "gemm_workspace",
-           "gemm_quantized", "gemm_bf16", "layer_is_quantized", "quantize_weight", "linear"]
+           "gemm_quantized", "gemm_bf16", "layer_is_quantized", "quantize_weight", "linear", "fp8_quantize", "fp8_gemm"]
 
 
 def _torch():
@@ -137,6 +138,35 @@ def gemm_quantized(a, w, amax, bias=None, epilogue="none", out=None):
                                                _ptr(codes), _ptr(scales), _ptr(ts), _stream()),
                    "nvfp4_gemm_quantized")
     return Nvfp4Tensor(codes, scales, ts, N)
+
+
+def fp8_quantize(x, dev_status=None, out=None):
+    """FP8 row-wise quantization of a 2-D bf16 tensor (one scale per row).
+    Returns an ``Fp8Tensor``; ``out``: optional (codes, scales)."""
+    torch = _torch()
+    rows, cols = x.shape
+    if out is None:
+        out = (torch.empty((rows, cols), dtype=torch.uint8, device=x.device),
+               torch.empty((rows,), dtype=torch.float32, device=x.device))
+    codes, scales = out
+    _binding.check(load().nvfp4_fp8_quantize_rowwise(_ptr(x), rows, cols, _ptr(codes), _ptr(scales),
+                                                     _ptr(dev_status), _stream()),
+                   "nvfp4_fp8_quantize_rowwise")
+    return Fp8Tensor(codes, scales)
+
+
+def fp8_gemm(a, w, bias=None, epilogue="none", out=None):
+    """Y = epi((A_q @ W_q^T) * dA[m] * dW[n] + bias) in bf16, from two ``Fp8Tensor``."""
+    torch = _torch()
+    M, K = a.codes.shape
+    N = w.codes.shape[0]
+    if w.codes.shape[1] != K:
+        raise ValueError("K mismatch")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.codes.device)
+    _binding.check(load().nvfp4_fp8_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(w.codes), _ptr(w.scales),
+                                         _ptr(bias), M, N, K, EPILOGUES[epilogue], _ptr(y), _stream()),
+                   "nvfp4_fp8_gemm")
+    return y
 
 
 def gemm_bf16(x, w, bias=None, epilogue="none", out=None):

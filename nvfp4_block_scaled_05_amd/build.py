@@ -33,7 +33,7 @@ DEVICE_FLAGS = [
 ]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-I", INCLUDE, "-Wall"]
 
-SOURCES = ["quantize.hip", "gemm_nvfp4.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm_nvfp4.hip", "gemm.hip", "fp8.hip", "api.cpp"]
 PROBE_SOURCES = ["isa_probe.hip"]     # test-only library of conversion probes
 
 

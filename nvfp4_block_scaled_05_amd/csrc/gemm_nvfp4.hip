@@ -44,8 +44,6 @@ namespace {
 constexpr int kBK = 128;               // K elements per step
 constexpr int kCodePitch = 80;         // LDS bytes per row of codes (64 used)
 constexpr int kScalePitch = 20;        // LDS bytes per row of fp16 scales (16 used)
-constexpr int kXcds = 8;
-constexpr int kGroupM = 8;
 
 // Tile shape BM x BN, WGM x WGN waves (each owns a WM x WN sub-tile of 32x32
 // MFMA tiles), MINB workgroups per CU requested from the register allocator.
@@ -403,36 +401,6 @@ __device__ __forceinline__ void finish_tile(const f32x16 (&acc)[C::TM][C::TN], f
     epilogue_quant<C>(acc, scale, bias, epi, M, N, m0, n0, out, lds);
   else
     epilogue<C>(acc, scale, bias, epi, M, N, m0, n0, out.y, out.y_amax);
-}
-
-// Position, in XCD-contiguous order, of workgroup b among the first T
-// workgroups: they are dealt to the XCDs round-robin, so the ones on XCD k
-// (b % 8 == k) take the k-th contiguous range of positions.
-__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t T) {
-  const int64_t xcd = b % kXcds, slot = b / kXcds;
-  // workgroups with id % 8 == k: n_k = ceil((T - k) / 8); start_k = sum_{j<k} n_j
-  int64_t start = 0;
-  for (int64_t k = 0; k < xcd; ++k) start += (T - k + kXcds - 1) / kXcds;
-  return start + slot;
-}
-
-// Tile (tm, tn) at position t of the row-grouped order: groups of kGroupM
-// tile-rows, column-major inside a group, so neighbours share A and W panels.
-__device__ __forceinline__ void grouped_tile(int64_t t, int64_t tiles_m, int64_t tiles_n,
-                                             int64_t& tm, int64_t& tn) {
-  const int64_t per_group = kGroupM * tiles_n;
-  const int64_t group = t / per_group;
-  const int64_t first_m = group * kGroupM;
-  const int64_t gsize = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
-  const int64_t in_group = t - group * per_group;
-  tm = first_m + in_group % gsize;
-  tn = in_group / gsize;
-}
-
-// Tile index of this workgroup: XCD-contiguous ranges, then row-grouped order.
-__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm,
-                                            int64_t& tn) {
-  grouped_tile(xcd_order(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 template <class C>

@@ -40,6 +40,13 @@ hipError_t launch_gemm_nvfp4_quantized(const uint8_t* a_codes, const uint8_t* a_
 // (0: no split for this shape).
 size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+// The FP8 row-wise variant.
+hipError_t launch_fp8_quantize_rowwise(const void* x, int64_t rows, int64_t cols, uint8_t* codes,
+                                       float* row_scales, int32_t* dev_status, hipStream_t stream);
+hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_codes,
+                           const float* w_scales, const void* bias, int64_t M, int64_t N,
+                           int64_t K, int epilogue, void* y, hipStream_t stream);
+
 hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, int64_t M, int64_t N,
                             int64_t K, int epilogue, void* y, hipStream_t stream);
 

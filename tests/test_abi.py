@@ -34,14 +34,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
         assert n in _binding.SIGNATURES, n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.nvfp4_abi_version() == 3
+    assert lib.nvfp4_abi_version() == 4
     for code in range(-8, 1):
         assert lib.nvfp4_status_string(code)
     assert lib.nvfp4_status_string(-99) == b"unknown status"
@@ -140,6 +140,20 @@ def test_gemm_quantized_argument_errors(lib):
     assert gq(yt=A + 2) == ALIGN
     assert gq(epi=5) == ARG
     assert gq(M=0, amax=None, yc=None, ys=None, yt=None) in (OK, DEVICE)
+
+
+def test_fp8_argument_errors(lib):
+    fq = lib.nvfp4_fp8_quantize_rowwise
+    assert fq(None, 4, 32, A, A, None, None) == NULL
+    assert fq(A, 4, 24, A, A, None, None) == SHAPE
+    assert fq(A + 8, 4, 32, A, A, None, None) == ALIGN
+    assert fq(A, 4, 32, A + 4, A, None, None) == ALIGN
+    fg = lib.nvfp4_fp8_gemm
+    assert fg(A, A, A, A, None, 8, 8, 64, 0, None, None) == NULL
+    assert fg(A, A, A, A, None, 8, 8, 40, 0, A, None) == SHAPE
+    assert fg(A + 8, A, A, A, None, 8, 8, 64, 0, A, None) == ALIGN
+    assert fg(A, A, A, A, None, 8, 8, 64, 9, A, None) == ARG
+    assert fg(A, A, A, A, None, 8, 8, 64, 0, A, None) in (OK, DEVICE)
 
 
 def test_layer_predicate_matches_python_re(lib):
