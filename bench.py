@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 TOKENS, HIDDEN, MLP = 16896, 3072, 12288
 GEMM_FLOP = 2 * TOKENS * MLP * HIDDEN              # each of up and down
 PEAK_MFMA_F16 = 2500.0                              # TFLOP/s, dense fp16/bf16 MFMA
+PEAK_MFMA_FP8 = 5000.0                              # TFLOP/s, dense fp8 MFMA
 PEAK_HBM = 8000.0                                   # GB/s
 QUANT_BYTES_PER_ELEM = 2 + 0.5 + 1.0 / 16           # bf16 read + codes + scales
 
@@ -207,6 +208,50 @@ def main():
                             for j, n in enumerate(["quantize_x_one_pass", "gemm_up_gelu_to_nvfp4",
                                                    "gemm_down"])}}
 
+    # the FP8 row-wise variant ("fp8r") of the same step: per-token activation
+    # scales, per-channel weight scales, native FP8 matrix cores
+    fw_up, fw_down = nv.fp8_quantize(w_up), nv.fp8_quantize(w_down)
+    fx = nv.fp8_quantize(x)
+    h8 = nv.fp8_gemm(fx, fw_up, epilogue="gelu")
+    fhq = nv.fp8_quantize(h8)
+    y8 = nv.fp8_gemm(fhq, fw_down)
+
+    def fp8_step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        nv.fp8_quantize(x, out=(fx.codes, fx.scales))
+        if events is not None:
+            events[1].record(stream)
+        nv.fp8_gemm(fx, fw_up, epilogue="gelu", out=h8)
+        if events is not None:
+            events[2].record(stream)
+        nv.fp8_quantize(h8, out=(fhq.codes, fhq.scales))
+        if events is not None:
+            events[3].record(stream)
+        nv.fp8_gemm(fhq, fw_down, out=y8)
+        if events is not None:
+            events[4].record(stream)
+
+    for _ in range(args.warmup):
+        fp8_step()
+    torch.cuda.synchronize()
+    fev = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    t_f = time.perf_counter()
+    for i in range(args.steps):
+        fp8_step(fev[i])
+    torch.cuda.synchronize()
+    fp8_ms = (time.perf_counter() - t_f) * 1e3 / args.steps
+    fst = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in fev]))
+           for j, n in enumerate(["quantize_x", "gemm_up_gelu", "quantize_h", "gemm_down"])}
+    fp8 = {"workload": "same step, FP8 row-wise (per-token / per-channel E4M3, native FP8 MFMA)",
+           "ms_per_step": round(fp8_ms, 4),
+           "TFLOPs": round(2 * GEMM_FLOP / (fp8_ms * 1e-3) / 1e12, 1),
+           "stages_us": {k: round(v, 2) for k, v in fst.items()},
+           "roofline_gemm_up": {"bound": "mfma", "peak": PEAK_MFMA_FP8, "unit": "TFLOP/s",
+                                "achieved": round(GEMM_FLOP / (fst["gemm_up_gelu"] * 1e-6) / 1e12, 1),
+                                "frac": round(GEMM_FLOP / (fst["gemm_up_gelu"] * 1e-6) / 1e12 / PEAK_MFMA_FP8, 4)},
+           "quantize_x_GBps": round(TOKENS * HIDDEN * 3 / fst["quantize_x"] / 1e3, 1)}
+
     # roofline of the dominant kernel: the up GEMM
     up_us = stage_us["gemm_up_gelu_amax"]
     achieved = GEMM_FLOP / (up_us * 1e-6) / 1e12
@@ -296,6 +341,7 @@ def main():
         "quantize": quant,
         "bf16_passthrough": bf16_pass,
         "static_scale": static,
+        "fp8_rowwise": fp8,
         "graphs": graphs,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),

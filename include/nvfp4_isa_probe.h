@@ -20,7 +20,10 @@ extern "C" {
 /* which = 0: E2M1 encode of binary32 patterns through the packed conversion
  *            (all four byte positions, both nibbles; a disagreement between
  *            them increments *mismatch);
- * which = 1: E4M3 encode of binary32 patterns (the quantizer's block scale).
+ * which = 1: E4M3 encode of binary32 patterns (the quantizer's block scale);
+ * which = 2: E4M3 encode of the FP8 row quantizer (min(v, 448) through the
+ *            packed hardware conversion, all four byte positions; a
+ *            disagreement between them increments *mismatch).
  * Scans the bit patterns lo .. lo + 256*nchunks (must not pass 2^32 - 1) and
  * appends every pattern p whose code differs from that of p - 1 to `list` as
  * the triple (p, code(p-1), code(p)), up to `cap` triples; *count receives the

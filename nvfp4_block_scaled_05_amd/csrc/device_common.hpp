@@ -35,11 +35,21 @@ __device__ __forceinline__ u16x2 max_u16x2(u16x2 a, u16x2 b) {
 // significand is rounded to 3 bits, nearest-even, by integer arithmetic, and
 // the exponent is rebiased from 127 to 7.
 __device__ __forceinline__ uint32_t e4m3_from_f32_rne(float t) {
-  if (t < 0.015625f) return (uint32_t)__builtin_rintf(t * 512.0f);
-  uint32_t u = __float_as_uint(t);
-  uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
-  uint32_t byte = ((((r >> 23) - 127u + 7u)) << 3) | ((r >> 20) & 7u);
-  return byte > 0x7Eu ? 0x7Eu : byte;
+  // both candidates are computed and one selected: no divergent branch
+  const uint32_t sub = (uint32_t)__builtin_rintf(t * 512.0f);
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  const uint32_t byte = ((((r >> 23) - 127u + 7u)) << 3) | ((r >> 20) & 7u);
+  return t < 0.015625f ? sub : (byte > 0x7Eu ? 0x7Eu : byte);
+}
+
+// E4M3 bytes of four values in [0, 448] through the gfx950 packed FP8
+// conversion (OCP E4M3, nearest-even); v0 lands in the low byte.  Callers
+// clamp to 448, which makes the conversion saturate exactly like
+// e4m3_from_f32_rne.
+__device__ __forceinline__ uint32_t e4m3_pack4(float v0, float v1, float v2, float v3) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
 }
 
 // E4M3 scale byte (0x00..0x7E: non-negative, finite) -> exact binary32.

@@ -9,10 +9,10 @@
 //
 //   Y[m,n] = bf16( epi( (sum_k qA[m,k] * qW[n,k]) * (dA[m] * dW[n]) + bias[n] ) ).
 //
-// Quantize: one wave per row.  The row max needs no other row, so the input
-// is read once from HBM (the encode pass re-reads the row from cache); the
-// E4M3 encoder is the integer round-to-nearest-even one of the NVFP4 block
-// scales.  GEMM: gfx950 runs E4M3 x E4M3 on the matrix cores natively
+// Quantize: a row's max needs no other row, so a workgroup holds its row in
+// registers and reads it from HBM once; the E4M3 encode is the gfx950 packed
+// conversion on values clamped to 448 (pinned against the oracle's encoder
+// over every binary32 pattern).  GEMM: gfx950 runs E4M3 x E4M3 on the matrix cores natively
 // (v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales), so unlike NVFP4
 // nothing is decoded: operand bytes go from HBM through LDS into the MFMA.
 #include "device_common.hpp"
@@ -28,16 +28,16 @@ typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kQThreads = 256;
 
-// E4M3 bytes of 4 bf16 values (two words) times s, sign in bit 7.
+// E4M3 bytes of 4 bf16 values (two words) times s, sign in bit 7: |x| * s in
+// binary32, clamped to 448 (saturation), then the packed hardware conversion.
 __device__ __forceinline__ uint32_t encode4_fp8(uint32_t w0, uint32_t w1, float s) {
-  const uint32_t h[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
-  uint32_t out = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float v = __uint_as_float((h[i] & 0x7FFFu) << 16) * s;
-    out |= (e4m3_from_f32_rne(v) | ((h[i] >> 8) & 0x80u)) << (8 * i);
-  }
-  return out;
+  const float v0 = __builtin_fminf(__uint_as_float((w0 & 0x7FFFu) << 16) * s, 448.0f);
+  const float v1 = __builtin_fminf(__uint_as_float(w0 & 0x7FFF0000u) * s, 448.0f);
+  const float v2 = __builtin_fminf(__uint_as_float((w1 & 0x7FFFu) << 16) * s, 448.0f);
+  const float v3 = __builtin_fminf(__uint_as_float(w1 & 0x7FFF0000u) * s, 448.0f);
+  const uint32_t signs = ((w0 >> 8) & 0x80u) | ((w0 >> 16) & 0x8000u) | ((w1 << 8) & 0x800000u) |
+                         (w1 & 0x80000000u);
+  return e4m3_pack4(v0, v1, v2, v3) | signs;
 }
 
 __global__ __launch_bounds__(kQThreads) void fp8_quantize_rowwise_kernel(
@@ -68,6 +68,51 @@ __global__ __launch_bounds__(kQThreads) void fp8_quantize_rowwise_kernel(
   for (int64_t k = (int64_t)lane * 8; k < cols; k += 512) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(xr + k);
     *reinterpret_cast<u32x2*>(cr + k) = u32x2{encode4_fp8(v.x, v.y, s), encode4_fp8(v.z, v.w, s)};
+  }
+}
+
+// One workgroup per row, the row held in registers (chunks of 8 elements,
+// thread t holding chunks t, t + 256, ...; indices past the row's end are
+// clamped to its last chunk, which leaves the max unchanged and is not
+// stored): the input is read from HBM exactly once.  Rows of up to
+// 2048 * MAXC elements.
+template <int MAXC>
+__global__ __launch_bounds__(kQThreads) void fp8_quantize_row_resident_kernel(
+    const uint16_t* __restrict__ x, int64_t cols, uint8_t* __restrict__ codes,
+    float* __restrict__ row_scales, int32_t* __restrict__ dev_status) {
+  __shared__ uint32_t red[kQThreads / 64];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int nch = (int)(cols / 8);
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + row * cols);
+  u32x4 v[MAXC];
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = min(tid + i * kQThreads, nch - 1);
+    v[i] = __builtin_nontemporal_load(xr + c);
+    m = max_u16x2(m, max8(v[i]));
+  }
+  const uint32_t wm = wave_max_u32(m.x > m.y ? m.x : m.y);
+  if ((tid & 63) == 0) red[tid >> 6] = wm;
+  __syncthreads();
+  const uint32_t amax_bits = max(max(red[0], red[1]), max(red[2], red[3])) << 16;
+  if (amax_bits >= 0x7F800000u) {                 // Inf / NaN in the row
+    if (tid == 0) {
+      row_scales[row] = __uint_as_float(0x7FC00000u);
+      if (dev_status) *dev_status = -8;           // NVFP4_ERR_NONFINITE
+    }
+    return;
+  }
+  const float amax = __uint_as_float(amax_bits);
+  const bool degenerate = amax < 0x1p-96f;
+  const float s = degenerate ? 1.0f : 448.0f / amax;
+  if (tid == 0) row_scales[row] = degenerate ? 1.0f : 1.0f / s;
+  u32x2* cr = reinterpret_cast<u32x2*>(codes + row * cols);
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = tid + i * kQThreads;
+    if (c < nch) cr[c] = u32x2{encode4_fp8(v[i].x, v[i].y, s), encode4_fp8(v[i].z, v[i].w, s)};
   }
 }
 
@@ -235,6 +280,18 @@ hipError_t launch_fp8_quantize_rowwise(const void* x, int64_t rows, int64_t cols
     if (e != hipSuccess) return e;
   }
   if (rows == 0) return hipSuccess;
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  if (cols <= 2048 * 2) {
+    hipLaunchKernelGGL(fp8_quantize_row_resident_kernel<2>, dim3((unsigned)rows), dim3(kQThreads),
+                       0, stream, xb, cols, codes, row_scales, dev_status);
+    return hipGetLastError();
+  }
+  if (cols <= 2048 * 6) {
+    hipLaunchKernelGGL(fp8_quantize_row_resident_kernel<6>, dim3((unsigned)rows), dim3(kQThreads),
+                       0, stream, xb, cols, codes, row_scales, dev_status);
+    return hipGetLastError();
+  }
+  // longer rows: a wave per row, the encode pass re-reading the row
   const int64_t wgs = (rows + kQThreads / 64 - 1) / (kQThreads / 64);
   hipLaunchKernelGGL(fp8_quantize_rowwise_kernel, dim3((unsigned)wgs), dim3(kQThreads), 0, stream,
                      reinterpret_cast<const uint16_t*>(x), rows, cols, codes, row_scales,

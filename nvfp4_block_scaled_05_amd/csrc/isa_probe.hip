@@ -8,6 +8,8 @@
 //     code changes characterises it completely.  All four byte positions of
 //     the packed conversion are exercised and must agree.
 //   * E4M3 encode (quantizer, integer arithmetic): the same scan.
+//   * E4M3 encode of the FP8 row quantizer (clamp to 448, packed hardware
+//     conversion): the same scan, all four byte positions.
 //   * E2M1 decode to fp16 / fp32 and E4M3 decode to fp16 / fp32 (GEMM
 //     loader, dequantizer): every byte value in every byte position.
 #include "device_common.hpp"
@@ -28,8 +30,13 @@ __device__ __forceinline__ uint32_t probe_code(uint32_t bits) {
     w = e2m1_pack2<2>(w, v, v);
     w = e2m1_pack2<3>(w, v, v);
     return w;   // 8 nibbles that must all be equal
-  } else {
+  } else if constexpr (MODE == 1) {
     return e4m3_from_f32_rne(v);
+  } else {
+    // the FP8 row quantizer's element encode: clamp to 448, then the packed
+    // conversion; the same value in all four byte positions
+    const float c = __builtin_fminf(v, 448.0f);
+    return e4m3_pack4(c, c, c, c);
   }
 }
 
@@ -47,6 +54,9 @@ __global__ __launch_bounds__(256) void transitions_kernel(uint32_t lo, uint32_t 
     if constexpr (MODE == 0) {
       if (c != (c & 0xFu) * 0x11111111u) atomicAdd(mismatch, 1u);
       c &= 0xFu;
+    } else if constexpr (MODE == 2) {
+      if (c != (c & 0xFFu) * 0x01010101u) atomicAdd(mismatch, 1u);
+      c &= 0xFFu;
     }
     if (i > 0 && c != prev) {
       const uint32_t slot = atomicAdd(count, 1u);
@@ -115,26 +125,30 @@ extern "C" {
 int nvfp4_probe_transitions(int which, uint32_t lo, uint32_t nchunks, uint32_t* list, uint32_t cap,
                             uint32_t* count, uint32_t* mismatch, void* stream) {
   if (bad_ptr(list) || bad_ptr(count) || bad_ptr(mismatch)) return -1;
-  if (which < 0 || which > 1 || nchunks == 0 || (uint64_t)lo + (uint64_t)nchunks * 256u > 0xFFFFFFFFull)
+  if (which < 0 || which > 2 || nchunks == 0 || (uint64_t)lo + (uint64_t)nchunks * 256u > 0xFFFFFFFFull)
     return -2;
   const dim3 grid((nchunks + 255) / 256), block(256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (which == 0)
     hipLaunchKernelGGL(transitions_kernel<0>, grid, block, 0, s, lo, nchunks, list, cap, count, mismatch);
-  else
+  else if (which == 1)
     hipLaunchKernelGGL(transitions_kernel<1>, grid, block, 0, s, lo, nchunks, list, cap, count, mismatch);
+  else
+    hipLaunchKernelGGL(transitions_kernel<2>, grid, block, 0, s, lo, nchunks, list, cap, count, mismatch);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
 int nvfp4_probe_encode(int which, const uint32_t* bits, int n, uint32_t* out, void* stream) {
   if (bad_ptr(bits) || bad_ptr(out)) return -1;
-  if (which < 0 || which > 1 || n <= 0) return -2;
+  if (which < 0 || which > 2 || n <= 0) return -2;
   const dim3 grid((n + 255) / 256), block(256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (which == 0)
     hipLaunchKernelGGL(encode_kernel<0>, grid, block, 0, s, bits, n, out);
-  else
+  else if (which == 1)
     hipLaunchKernelGGL(encode_kernel<1>, grid, block, 0, s, bits, n, out);
+  else
+    hipLaunchKernelGGL(encode_kernel<2>, grid, block, 0, s, bits, n, out);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

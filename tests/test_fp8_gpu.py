@@ -39,7 +39,9 @@ def check_fp8_quantize(bits, label=""):
     return q, ref
 
 
-SHAPES = [(1, 16), (3, 48), (37, 1040), (257, 3072), (5, 12288)]
+# rows up to 4096 and up to 12288 columns are held in registers; longer rows
+# take the wave-per-row path
+SHAPES = [(1, 16), (3, 48), (37, 1040), (257, 3072), (9, 4112), (5, 12288), (3, 12304), (2, 20000)]
 KINDS = ["normal", "t3", "outliers"]
 
 

@@ -134,6 +134,18 @@ def test_e4m3_encode_every_nonnegative_pattern(probe):
     assert list(_encode(probe, 1, anchors)) == list(_e4m3_code(anchors))
 
 
+def test_fp8_row_encode_every_nonnegative_pattern(probe):
+    # the FP8 row quantizer's element encode (clamp to 448, hardware packed
+    # conversion) has exactly the transitions of the oracle's E4M3 encoder
+    lo, hi = 0x00000000, 0x7F800000
+    got, mismatch = _scan(probe, 2, lo, hi)
+    assert mismatch == 0, "byte positions of the packed conversion disagree"
+    want = _expected_transitions(_e4m3_code, lo, hi)
+    assert got == want
+    anchors = np.array([lo, 0x3A800000, 0x3A800001, 0x43E00000, 0x43E80000, hi], np.uint32)
+    assert list(_encode(probe, 2, anchors) & 0xFF) == list(_e4m3_code(anchors))
+
+
 def test_decodes_every_byte_and_scale(probe):
     import torch
     # every byte value in every byte position, times every finite E4M3 scale
