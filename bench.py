@@ -27,6 +27,7 @@ import json
 import os
 import sys
 import time
+from types import SimpleNamespace
 
 import numpy as np
 
@@ -48,6 +49,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-graphs", action="store_true", help="skip the HIP-graph section")
+    p.add_argument("--no-extras", action="store_true",
+                   help="only the headline step, quantize and bf16 sections (profiling runs)")
     p.add_argument("--cpu-rows", type=int, default=12288)
     p.add_argument("--calib-copy", action="store_true")
     return p.parse_args()
@@ -172,85 +175,11 @@ def main():
                 for j, n in enumerate(stage_names)}
     value = 2 * GEMM_FLOP / (ms_per_step * 1e-3) / 1e12
 
-    # the same step under static (calibrated) tensor scales: X quantized in
-    # one pass, H written in NVFP4 by the up projection's epilogue (no bf16 H)
-    x_static = torch.tensor([float(x.float().abs().max())], dtype=torch.float32, device=dev)
-    h_static = amax.clone()                     # calibrated on the dynamic step
-    hq_s = nv.gemm_quantized(xq, wq_up, h_static, epilogue="gelu")
-    hq_s_out = (hq_s.codes, hq_s.scales, hq_s.tensor_scale)
-
-    def static_step(events=None):
-        if events is not None:
-            events[0].record(stream)
-        nv.quantize(x, amax=x_static, out=xq_out)
-        if events is not None:
-            events[1].record(stream)
-        nv.gemm_quantized(xq, wq_up, h_static, epilogue="gelu", out=hq_s_out)
-        if events is not None:
-            events[2].record(stream)
-        nv.gemm(hq_s, wq_down, out=y, workspace=ws_down)
-        if events is not None:
-            events[3].record(stream)
-
-    for _ in range(args.warmup):
-        static_step()
-    torch.cuda.synchronize()
-    sev = [[ev() for _ in range(4)] for _ in range(args.steps)]
-    t_s = time.perf_counter()
-    for i in range(args.steps):
-        static_step(sev[i])
-    torch.cuda.synchronize()
-    static_ms = (time.perf_counter() - t_s) * 1e3 / args.steps
-    static = {"workload": "same step with static tensor scales (calibrated amax of X and H)",
-              "ms_per_step": round(static_ms, 4),
-              "TFLOPs": round(2 * GEMM_FLOP / (static_ms * 1e-3) / 1e12, 1),
-              "stages_us": {n: round(float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in sev])), 2)
-                            for j, n in enumerate(["quantize_x_one_pass", "gemm_up_gelu_to_nvfp4",
-                                                   "gemm_down"])}}
-
-    # the FP8 row-wise variant ("fp8r") of the same step: per-token activation
-    # scales, per-channel weight scales, native FP8 matrix cores
-    fw_up, fw_down = nv.fp8_quantize(w_up), nv.fp8_quantize(w_down)
-    fx = nv.fp8_quantize(x)
-    h8 = nv.fp8_gemm(fx, fw_up, epilogue="gelu")
-    fhq = nv.fp8_quantize(h8)
-    y8 = nv.fp8_gemm(fhq, fw_down)
-
-    def fp8_step(events=None):
-        if events is not None:
-            events[0].record(stream)
-        nv.fp8_quantize(x, out=(fx.codes, fx.scales))
-        if events is not None:
-            events[1].record(stream)
-        nv.fp8_gemm(fx, fw_up, epilogue="gelu", out=h8)
-        if events is not None:
-            events[2].record(stream)
-        nv.fp8_quantize(h8, out=(fhq.codes, fhq.scales))
-        if events is not None:
-            events[3].record(stream)
-        nv.fp8_gemm(fhq, fw_down, out=y8)
-        if events is not None:
-            events[4].record(stream)
-
-    for _ in range(args.warmup):
-        fp8_step()
-    torch.cuda.synchronize()
-    fev = [[ev() for _ in range(5)] for _ in range(args.steps)]
-    t_f = time.perf_counter()
-    for i in range(args.steps):
-        fp8_step(fev[i])
-    torch.cuda.synchronize()
-    fp8_ms = (time.perf_counter() - t_f) * 1e3 / args.steps
-    fst = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in fev]))
-           for j, n in enumerate(["quantize_x", "gemm_up_gelu", "quantize_h", "gemm_down"])}
-    fp8 = {"workload": "same step, FP8 row-wise (per-token / per-channel E4M3, native FP8 MFMA)",
-           "ms_per_step": round(fp8_ms, 4),
-           "TFLOPs": round(2 * GEMM_FLOP / (fp8_ms * 1e-3) / 1e12, 1),
-           "stages_us": {k: round(v, 2) for k, v in fst.items()},
-           "roofline_gemm_up": {"bound": "mfma", "peak": PEAK_MFMA_FP8, "unit": "TFLOP/s",
-                                "achieved": round(GEMM_FLOP / (fst["gemm_up_gelu"] * 1e-6) / 1e12, 1),
-                                "frac": round(GEMM_FLOP / (fst["gemm_up_gelu"] * 1e-6) / 1e12 / PEAK_MFMA_FP8, 4)},
-           "quantize_x_GBps": round(TOKENS * HIDDEN * 3 / fst["quantize_x"] / 1e3, 1)}
+    extras = SimpleNamespace(x=x, xq=xq, xq_out=xq_out, wq_up=wq_up, wq_down=wq_down, amax=amax,
+                             y=y, ws_down=ws_down, w_up=w_up, w_down=w_down, stream=stream, ev=ev,
+                             steps=args.steps, warmup=args.warmup)
+    static = None if args.no_extras else static_section(extras)
+    fp8 = None if args.no_extras else fp8_section(extras)
 
     # roofline of the dominant kernel: the up GEMM
     up_us = stage_us["gemm_up_gelu_amax"]
@@ -317,7 +246,7 @@ def main():
                  "us": round(mod_us, 2),
                  "GBps_weight_read": round(6 * HIDDEN * HIDDEN * 2 / mod_us / 1e3, 1)}
 
-    graphs = None if args.no_graphs else graph_section(to_dev, ev, stream)
+    graphs = None if args.no_graphs or args.no_extras else graph_section(to_dev, ev, stream)
 
     # ----------------------------------------------------------- CPU oracle --
     cpu = None
@@ -347,6 +276,81 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(rec))
+
+
+def timed_sequence(c, fn, names):
+    """Warm up, then time c.steps runs of fn(events) (events bracket its
+    len(names) stages); returns (ms per run, {stage: mean us})."""
+    import torch
+    for _ in range(c.warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    evs = [[c.ev() for _ in range(len(names) + 1)] for _ in range(c.steps)]
+    t0 = time.perf_counter()
+    for i in range(c.steps):
+        fn(evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / c.steps
+    stages = {n: round(float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs])), 2)
+              for j, n in enumerate(names)}
+    return ms, stages
+
+
+def static_section(c):
+    """The step under static (calibrated) tensor scales: X quantized in one
+    pass, H written in NVFP4 by the up projection's epilogue (no bf16 H)."""
+    import torch
+    import nvfp4_block_scaled_05_amd as nv
+    x_static = torch.tensor([float(c.x.float().abs().max())], dtype=torch.float32, device=c.x.device)
+    h_static = c.amax.clone()                   # calibrated on the dynamic step
+    hq = nv.gemm_quantized(c.xq, c.wq_up, h_static, epilogue="gelu")
+    hq_out = (hq.codes, hq.scales, hq.tensor_scale)
+
+    def run(events):
+        mark = (lambda k: events[k].record(c.stream)) if events else (lambda k: None)
+        mark(0)
+        nv.quantize(c.x, amax=x_static, out=c.xq_out)
+        mark(1)
+        nv.gemm_quantized(c.xq, c.wq_up, h_static, epilogue="gelu", out=hq_out)
+        mark(2)
+        nv.gemm(hq, c.wq_down, out=c.y, workspace=c.ws_down)
+        mark(3)
+    ms, stages = timed_sequence(c, run, ["quantize_x_one_pass", "gemm_up_gelu_to_nvfp4", "gemm_down"])
+    return {"workload": "same step with static tensor scales (calibrated amax of X and H)",
+            "ms_per_step": round(ms, 4), "TFLOPs": round(2 * GEMM_FLOP / (ms * 1e-3) / 1e12, 1),
+            "stages_us": stages}
+
+
+def fp8_section(c):
+    """The FP8 row-wise variant ("fp8r") of the step: per-token activation
+    scales, per-channel weight scales, native FP8 matrix cores."""
+    import nvfp4_block_scaled_05_amd as nv
+    fw_up, fw_down = nv.fp8_quantize(c.w_up), nv.fp8_quantize(c.w_down)
+    fx = nv.fp8_quantize(c.x)
+    h8 = nv.fp8_gemm(fx, fw_up, epilogue="gelu")
+    fh = nv.fp8_quantize(h8)
+    y8 = nv.fp8_gemm(fh, fw_down)
+
+    def run(events):
+        mark = (lambda k: events[k].record(c.stream)) if events else (lambda k: None)
+        mark(0)
+        nv.fp8_quantize(c.x, out=(fx.codes, fx.scales))
+        mark(1)
+        nv.fp8_gemm(fx, fw_up, epilogue="gelu", out=h8)
+        mark(2)
+        nv.fp8_quantize(h8, out=(fh.codes, fh.scales))
+        mark(3)
+        nv.fp8_gemm(fh, fw_down, out=y8)
+        mark(4)
+    ms, st = timed_sequence(c, run, ["quantize_x", "gemm_up_gelu", "quantize_h", "gemm_down"])
+    up = GEMM_FLOP / (st["gemm_up_gelu"] * 1e-6) / 1e12
+    return {"workload": "same step, FP8 row-wise (per-token / per-channel E4M3, native FP8 MFMA)",
+            "ms_per_step": round(ms, 4), "TFLOPs": round(2 * GEMM_FLOP / (ms * 1e-3) / 1e12, 1),
+            "stages_us": st,
+            "roofline_gemm_up": {"bound": "mfma", "peak": PEAK_MFMA_FP8, "unit": "TFLOP/s",
+                                 "achieved": round(up, 1), "frac": round(up / PEAK_MFMA_FP8, 4)},
+            "quantize_x_GBps": round(TOKENS * HIDDEN * 3 / st["quantize_x"] / 1e3, 1),
+            "quantize_h_GBps": round(TOKENS * MLP * 3 / st["quantize_h"] / 1e3, 1)}
 
 
 def graph_section(to_dev, ev, stream):
