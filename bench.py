@@ -327,20 +327,23 @@ def fp8_section(c):
     import nvfp4_block_scaled_05_amd as nv
     fw_up, fw_down = nv.fp8_quantize(c.w_up), nv.fp8_quantize(c.w_down)
     fx = nv.fp8_quantize(c.x)
-    h8 = nv.fp8_gemm(fx, fw_up, epilogue="gelu")
+    dev = c.x.device
+    ws_up = nv.fp8_gemm_workspace(TOKENS, MLP, HIDDEN, device=dev)
+    ws_down = nv.fp8_gemm_workspace(TOKENS, HIDDEN, MLP, device=dev)
+    h8 = nv.fp8_gemm(fx, fw_up, epilogue="gelu", workspace=ws_up)
     fh = nv.fp8_quantize(h8)
-    y8 = nv.fp8_gemm(fh, fw_down)
+    y8 = nv.fp8_gemm(fh, fw_down, workspace=ws_down)
 
     def run(events):
         mark = (lambda k: events[k].record(c.stream)) if events else (lambda k: None)
         mark(0)
         nv.fp8_quantize(c.x, out=(fx.codes, fx.scales))
         mark(1)
-        nv.fp8_gemm(fx, fw_up, epilogue="gelu", out=h8)
+        nv.fp8_gemm(fx, fw_up, epilogue="gelu", out=h8, workspace=ws_up)
         mark(2)
         nv.fp8_quantize(h8, out=(fh.codes, fh.scales))
         mark(3)
-        nv.fp8_gemm(fh, fw_down, out=y8)
+        nv.fp8_gemm(fh, fw_down, out=y8, workspace=ws_down)
         mark(4)
     ms, st = timed_sequence(c, run, ["quantize_x", "gemm_up_gelu", "quantize_h", "gemm_down"])
     up = GEMM_FLOP / (st["gemm_up_gelu"] * 1e-6) / 1e12

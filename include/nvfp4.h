@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 4
+#define NVFP4_ABI_VERSION 5
 #define NVFP4_BLOCK 16 /* elements per block scale, [P1] "NVFP4量化" */
 
 typedef enum {
@@ -235,10 +235,27 @@ int nvfp4_fp8_quantize_rowwise(const void* x_bf16, int64_t rows, int64_t cols, u
  *   w_codes / w_scales  [N, K] / [N];  code pointers 16-byte aligned.
  *   bias_bf16 optional [N];  M, N >= 0, K > 0, K % 16 == 0.
  *   y_bf16 out [M, N] bf16, 2-byte aligned.
+ *   workspace  optional device scratch, 256-byte aligned, owned by the call
+ *              until it completes on `stream`; contents on entry irrelevant.
+ *              With at least nvfp4_fp8_gemm_workspace_bytes(M, N, K) bytes the
+ *              tiles past the last whole round of workgroups over the compute
+ *              units are split over K and their fp32 partial sums added there,
+ *              in a fixed order, by a second kernel on `stream`; NULL or a
+ *              smaller size computes every tile whole.  Either way the result
+ *              is deterministic; the two differ only in the order of the fp32
+ *              additions.
  */
 int nvfp4_fp8_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_codes,
                    const float* w_scales, const void* bias_bf16, int64_t M, int64_t N, int64_t K,
-                   int epilogue, void* y_bf16, void* stream);
+                   int epilogue, void* y_bf16, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * nvfp4_fp8_gemm_workspace_bytes -- workspace bytes nvfp4_fp8_gemm can use for
+ * an (M, N, K) problem on the current device (0: it would not split).  Host
+ * only; at most 256 KiB per compute unit (64 MiB on a 256-CU device).
+ */
+size_t nvfp4_fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * nvfp4_gemm_bf16 -- the bf16 passthrough for layers kept in higher precision

@@ -19,7 +19,8 @@ Fp8Tensor = namedtuple("Fp8Tensor", ["codes", "scales"])   # E4M3 [rows, cols], 
 
 __all__ = ["Nvfp4Tensor", "Fp8Tensor", "Nvfp4Error", "load", "abi_version", "status_string",
            "quantize_workspace_bytes", "quantize", "dequantize", "gemm", "gemm_workspace",
-           "gemm_quantized", "gemm_bf16", "layer_is_quantized", "quantize_weight", "linear", "fp8_quantize", "fp8_gemm"]
+           "gemm_quantized", "gemm_bf16", "layer_is_quantized", "quantize_weight", "linear",
+           "fp8_quantize", "fp8_gemm", "fp8_gemm_workspace"]
 
 
 def _torch():
@@ -155,16 +156,31 @@ def fp8_quantize(x, dev_status=None, out=None):
     return Fp8Tensor(codes, scales)
 
 
-def fp8_gemm(a, w, bias=None, epilogue="none", out=None):
-    """Y = epi((A_q @ W_q^T) * dA[m] * dW[n] + bias) in bf16, from two ``Fp8Tensor``."""
+def fp8_gemm_workspace(M, N, K, device="cuda"):
+    """A workspace for ``fp8_gemm`` on an (M, N, K) problem, or None if it would not split."""
+    nbytes = load().nvfp4_fp8_gemm_workspace_bytes(M, N, K)
+    if nbytes == 0:
+        return None
+    return _torch().empty(nbytes, dtype=_torch().uint8, device=device)
+
+
+def fp8_gemm(a, w, bias=None, epilogue="none", out=None, workspace=_NO_WORKSPACE):
+    """Y = epi((A_q @ W_q^T) * dA[m] * dW[n] + bias) in bf16, from two ``Fp8Tensor``.
+
+    ``workspace``: as for ``gemm`` (from ``fp8_gemm_workspace``, None, or left out).
+    """
     torch = _torch()
     M, K = a.codes.shape
     N = w.codes.shape[0]
     if w.codes.shape[1] != K:
         raise ValueError("K mismatch")
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.codes.device)
+    if workspace is _NO_WORKSPACE:
+        workspace = fp8_gemm_workspace(M, N, K, device=a.codes.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _binding.check(load().nvfp4_fp8_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(w.codes), _ptr(w.scales),
-                                         _ptr(bias), M, N, K, EPILOGUES[epilogue], _ptr(y), _stream()),
+                                         _ptr(bias), M, N, K, EPILOGUES[epilogue], _ptr(y),
+                                         _ptr(workspace), ws_bytes, _stream()),
                    "nvfp4_fp8_gemm")
     return y
 

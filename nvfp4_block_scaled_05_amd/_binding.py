@@ -35,7 +35,9 @@ SIGNATURES = {
                                             ctypes.c_int, _P, _P, _P, _P, _P]),
     "nvfp4_gemm_bf16": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
     "nvfp4_fp8_quantize_rowwise": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
-    "nvfp4_fp8_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
+    "nvfp4_fp8_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P,
+                                      ctypes.c_size_t, _P]),
+    "nvfp4_fp8_gemm_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "nvfp4_layer_is_quantized": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_char_p]),
 }
 

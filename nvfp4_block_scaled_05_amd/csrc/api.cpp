@@ -179,23 +179,32 @@ int nvfp4_fp8_quantize_rowwise(const void* x_bf16, int64_t rows, int64_t cols, u
                                                        static_cast<hipStream_t>(stream)));
 }
 
+size_t nvfp4_fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K) || K % 16 != 0) return 0;
+  return nvfp4::gemm_fp8_workspace_bytes(M, N, K);
+}
+
 int nvfp4_fp8_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_codes,
                    const float* w_scales, const void* bias_bf16, int64_t M, int64_t N, int64_t K,
-                   int epilogue, void* y_bf16, void* stream) {
+                   int epilogue, void* y_bf16, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return NVFP4_ERR_SHAPE;
   const bool empty = M == 0 || N == 0;
   if (!empty && (!a_codes || !a_scales || !w_codes || !w_scales || !y_bf16)) return NVFP4_ERR_NULL;
   if (K == 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
   if (((M + 255) / 256) * ((N + 255) / 256) >= ((int64_t)1 << 24)) return NVFP4_ERR_SHAPE;
   if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_scales, 4) ||
-      !aligned(w_scales, 4) || !aligned(bias_bf16, 2) || !aligned(y_bf16, 2))
+      !aligned(w_scales, 4) || !aligned(bias_bf16, 2) || !aligned(y_bf16, 2) ||
+      !aligned(workspace, 256))
     return NVFP4_ERR_ALIGN;
   if (epilogue != NVFP4_EPI_NONE && epilogue != NVFP4_EPI_GELU) return NVFP4_ERR_ARG;
   int st = check_device();
   if (st != NVFP4_OK) return st;
   if (empty) return NVFP4_OK;
   return hip_status(nvfp4::launch_gemm_fp8(a_codes, a_scales, w_codes, w_scales, bias_bf16, M, N,
-                                           K, epilogue, y_bf16, static_cast<hipStream_t>(stream)));
+                                           K, epilogue, y_bf16, workspace,
+                                           workspace ? workspace_bytes : 0,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int nvfp4_gemm_bf16(const void* x_bf16, const void* w_bf16, const void* bias_bf16, int64_t M,

@@ -241,6 +241,34 @@ __device__ __forceinline__ void grouped_tile(int64_t t, int64_t tiles_m, int64_t
   tn = in_group / gsize;
 }
 
+// Split K for the tail of a tiled GEMM: workgroups 0 .. main_tiles-1 compute
+// whole tiles; the remaining tiles are each split into `ways` ranges of K
+// stages, one workgroup per range, whose fp32 partial sums go to their own
+// slice of `part` for a second kernel to add in split order.
+struct SplitK {
+  float* part;         // [tail tiles][ways][BM][BN] fp32 partial sums
+  int64_t main_tiles;  // tiles computed whole, by workgroups 0 .. main_tiles-1
+  int ways;            // K ranges per tail tile (1: no split)
+};
+
+// Work of this workgroup: tile (tm, tn), and for a tail tile its index among
+// the tail tiles and its split (split < 0 for a whole tile).
+__device__ __forceinline__ void split_coords(int64_t tiles_m, int64_t tiles_n, const SplitK& sk,
+                                             int64_t& tm, int64_t& tn, int64_t& tail,
+                                             int& split) {
+  const int64_t b = blockIdx.x;
+  if (b < sk.main_tiles) {
+    grouped_tile(xcd_order(b, sk.main_tiles), tiles_m, tiles_n, tm, tn);
+    tail = -1;
+    split = -1;
+  } else {
+    const int64_t u = b - sk.main_tiles;
+    tail = u / sk.ways;
+    split = (int)(u - tail * sk.ways);
+    grouped_tile(sk.main_tiles + tail, tiles_m, tiles_n, tm, tn);
+  }
+}
+
 // Tile index of this workgroup: XCD-contiguous ranges, then row-grouped order.
 __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm,
                                             int64_t& tn) {

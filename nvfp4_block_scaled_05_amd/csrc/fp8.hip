@@ -15,6 +15,10 @@
 // over every binary32 pattern).  GEMM: gfx950 runs E4M3 x E4M3 on the matrix cores natively
 // (v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales), so unlike NVFP4
 // nothing is decoded: operand bytes go from HBM through LDS into the MFMA.
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -269,6 +273,300 @@ __global__ __launch_bounds__(kNT, 1) void gemm_fp8_kernel(
   }
 }
 
+// ------------------------------------------------- GEMM, direct-to-LDS --
+//
+// For K % 128 == 0.  Workgroup of 4 waves in 2x2 over a 256x256 tile, each
+// wave 128x128 (4x4 MFMA tiles, 256 fp32 accumulators per lane): half the LDS
+// reads per flop of the 8-wave layout above.  K advances 128 per stage (two
+// MFMA k-steps of 64), double-buffered in LDS (2 x 64 KB).
+//   * Operand bytes go from global memory straight into LDS (the gfx950
+//     16-byte global->LDS load: one instruction fills 1 KB, lane L's 16 bytes
+//     at offset 16 L), so they pass through no registers.  One instruction
+//     covers 8 rows x 128 bytes; inside a row the 16-byte pieces are permuted
+//     by an XOR with (row / 2) % 8, which makes every fragment read below
+//     (16 lanes, 16 consecutive rows, the same logical piece) touch 16
+//     different bank groups.
+//   * Fragments: lane (r = lane % 32, h = lane / 32) of an MFMA takes 32 bytes
+//     of row r: pieces 4s + 2h and 4s + 2h + 1 for k-step s.  A and W use the
+//     same order, so the sum over k is the same.
+//   * Each stage has one barrier; the MFMAs of its second k-step run after
+//     the next barrier, while the first LDS reads of the next stage are in
+//     flight, so the matrix pipe does not drain at every barrier.
+// Rows past M or N are read clamped to the last row (valid memory); their
+// results are never stored.
+constexpr int kDBM = 256, kDBN = 256, kDBK = 128, kDNT = 256;
+constexpr int kDWM = 128, kDWN = 128, kDTM = kDWM / 32, kDTN = kDWN / 32;
+constexpr int kDOp = kDBM * kDBK;          // bytes of one operand per stage
+constexpr int kDStage = 2 * kDOp;          // A then W
+
+// This lane's source offsets (bytes from the operand's start; rows * K
+// < 2^32 is checked on the host), one per 8-row chunk it loads.
+struct DmaPtrs {
+  uint32_t a[kDBM / 8 / 4];
+  uint32_t w[kDBN / 8 / 4];
+};
+
+__device__ __forceinline__ void dma_setup(int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                          DmaPtrs& d) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < kDBM / 8 / 4; ++i) {
+    const int c = wave * (kDBM / 8 / 4) + i;             // chunk: rows 8c .. 8c+7
+    const int row = 8 * c + (lane >> 3);
+    const int piece = (lane & 7) ^ ((row >> 1) & 7);
+    const int64_t ra = m0 + row < M ? m0 + row : M - 1;
+    const int64_t rw = n0 + row < N ? n0 + row : N - 1;
+    d.a[i] = (uint32_t)(ra * K + piece * 16);
+    d.w[i] = (uint32_t)(rw * K + piece * 16);
+  }
+}
+
+__device__ __forceinline__ void dma_issue(const uint8_t* __restrict__ a, const uint8_t* __restrict__ w,
+                                          const DmaPtrs& d, int64_t k0, uint8_t* stage) {
+  const int wave = threadIdx.x >> 6;
+  const uint8_t* ak = a + k0;
+  const uint8_t* wk = w + k0;
+#pragma unroll
+  for (int i = 0; i < kDBM / 8 / 4; ++i) {
+    const int c = wave * (kDBM / 8 / 4) + i;
+    __builtin_amdgcn_global_load_lds(ak + d.a[i], stage + c * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wk + d.w[i], stage + kDOp + c * 1024, 16, 0, 0);
+  }
+}
+
+struct DmaFrags {
+  i32x8 a[kDTM], b[kDTN];
+};
+
+// Fragments of k-step s from one stage.  row_off: this lane's byte offset of
+// its row in the wave's first A / W tile; sw = (row / 2) % 8.
+template <int S>
+__device__ __forceinline__ void dma_frags(const uint8_t* stage, int a_off, int b_off, int h, int sw,
+                                          DmaFrags& f) {
+  const int p0 = ((4 * S + 2 * h) ^ sw) << 4, p1 = ((4 * S + 2 * h + 1) ^ sw) << 4;
+#pragma unroll
+  for (int i = 0; i < kDTM; ++i) {
+    const uint8_t* r = stage + a_off + i * 32 * kDBK;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(r + p0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(r + p1);
+    f.a[i] = __builtin_bit_cast(i32x8, (u32x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+#pragma unroll
+  for (int j = 0; j < kDTN; ++j) {
+    const uint8_t* r = stage + kDOp + b_off + j * 32 * kDBK;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(r + p0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(r + p1);
+    f.b[j] = __builtin_bit_cast(i32x8, (u32x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+// The weight fragment is the MFMA's first operand and the activation the
+// second, so acc[i][j] holds the transposed 32x32 tile: lane (r, h) has row
+// m = i*32 + r of Y and columns n = j*32 + 8g + 4h + t at element 4g + t --
+// four consecutive columns of one row per g, stored as one 8-byte write.
+__device__ __forceinline__ void dma_mfma(const DmaFrags& f, f32x16 (&acc)[kDTM][kDTN]) {
+#pragma unroll
+  for (int i = 0; i < kDTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kDTN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0,
+                                                                   127, 0, 127);
+}
+
+// Every DMA of this wave has landed in LDS (vmcnt 0), then the workgroup
+// barrier: all waves' data for the next stage is visible and all reads of the
+// buffer about to be refilled are done.
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// One stage: refill `nxt` with the stage after this one (if any), read this
+// stage's fragments from `cur`, and run the previous stage's second k-step and
+// this stage's first.  MFMAs are interleaved with the LDS reads and the DMA
+// issues so that the reads' latency is covered by matrix work.
+__device__ __forceinline__ void dma_stage(const uint8_t* __restrict__ a, const uint8_t* __restrict__ w,
+                                          const uint8_t* cur, uint8_t* nxt, const DmaPtrs& ptr,
+                                          bool refill, int64_t k_next, int a_off, int b_off, int h,
+                                          int sw, DmaFrags& f0, DmaFrags& f1,
+                                          f32x16 (&acc)[kDTM][kDTN]) {
+  dma_barrier();
+  if (refill) dma_issue(a, w, ptr, k_next, nxt);
+  dma_frags<0>(cur, a_off, b_off, h, sw, f0);
+  dma_mfma(f1, acc);                        // previous stage, k-step 1
+  dma_frags<1>(cur, a_off, b_off, h, sw, f1);
+  dma_mfma(f0, acc);
+#pragma unroll
+  for (int m = 0; m < kDTM * kDTN; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (DMA issue)
+  }
+#pragma unroll
+  for (int m = 0; m < kDTM * kDTN; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+__global__ __launch_bounds__(kDNT, 1) void gemm_fp8_dma_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ da, const uint8_t* __restrict__ w,
+    const float* __restrict__ dw, const uint16_t* __restrict__ bias, int64_t M, int64_t N,
+    int64_t K, int epi, uint16_t* __restrict__ y, SplitK sk) {
+  // two separately declared buffers, so that reads of one are seen not to
+  // alias DMA writes into the other
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kDStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kDStage];
+  __shared__ float row_scale[kDBM];
+  __shared__ __attribute__((aligned(16))) float col_scale[kDBN], col_bias[kDBN];
+  const int64_t tiles_m = (M + kDBM - 1) / kDBM, tiles_n = (N + kDBN - 1) / kDBN;
+  int64_t tm, tn, tail;
+  int split;
+  split_coords(tiles_m, tiles_n, sk, tm, tn, tail, split);
+  const int64_t m0 = tm * kDBM, n0 = tn * kDBN;
+  {
+    const int64_t r = m0 + threadIdx.x, c = n0 + threadIdx.x;
+    row_scale[threadIdx.x] = r < M ? da[r] : 0.0f;
+    col_scale[threadIdx.x] = c < N ? dw[c] : 0.0f;
+    col_bias[threadIdx.x] = (bias && c < N) ? bf16_bits_to_f32(bias[c]) : 0.0f;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, h = lane >> 5, sw = (r >> 1) & 7;
+  const int a_off = (wm * kDWM + r) * kDBK, b_off = (wn * kDWN + r) * kDBK;
+
+  DmaPtrs ptr;
+  dma_setup(M, N, K, m0, n0, ptr);
+  f32x16 acc[kDTM][kDTN];
+#pragma unroll
+  for (int i = 0; i < kDTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kDTN; ++j) acc[i][j] = f32x16{};
+
+  // stages [kb, ke) of 128 K: all of them, or this split's share
+  const int nk = (int)(K / kDBK);
+  const int kb = split < 0 ? 0 : (int)((int64_t)split * nk / sk.ways);
+  const int ke = split < 0 ? nk : (int)((int64_t)(split + 1) * nk / sk.ways);
+  const int ns = ke - kb;
+  DmaFrags f0, f1;
+  dma_issue(a, w, ptr, (int64_t)kb * kDBK, lds0);
+  dma_barrier();
+  if (ns > 1) dma_issue(a, w, ptr, (int64_t)(kb + 1) * kDBK, lds1);
+  dma_frags<0>(lds0, a_off, b_off, h, sw, f0);
+  dma_frags<1>(lds0, a_off, b_off, h, sw, f1);
+  dma_mfma(f0, acc);
+  // stage kb + t reads buffer t % 2 and refills the other with stage kb + t + 1;
+  // whole pairs of stages, then at most one more
+  int t = 1;
+  for (; t + 1 < ns; t += 2) {
+    dma_stage(a, w, lds1, lds0, ptr, true, (int64_t)(kb + t + 1) * kDBK, a_off, b_off, h, sw, f0,
+              f1, acc);
+    dma_stage(a, w, lds0, lds1, ptr, t + 2 < ns, (int64_t)(kb + t + 2) * kDBK, a_off, b_off, h, sw,
+              f0, f1, acc);
+  }
+  if (t < ns)
+    dma_stage(a, w, lds1, lds0, ptr, false, 0, a_off, b_off, h, sw, f0, f1, acc);
+  dma_mfma(f1, acc);
+
+  if (split >= 0) {
+    // a tail split: fp32 partial sums into its slice in accumulator order --
+    // float4 number (((wave * 4 + i) * 4 + j) * 64 + lane) * 4 + g holds
+    // acc[i][j][4g .. 4g+3], so each wave writes 4 KB contiguous per tile
+    f32x4* slice = reinterpret_cast<f32x4*>(sk.part + (tail * sk.ways + split) * (int64_t)(kDBM * kDBN));
+#pragma unroll
+    for (int i = 0; i < kDTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kDTN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          slice[(((wave * kDTM + i) * kDTN + j) * 64 + lane) * 4 + g] =
+              f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    return;
+  }
+
+  // epilogue: (acc * (dA[m] * dW[n]) + bias) -> GELU -> bf16 (the operations
+  // of gemm_fp8_kernel's epilogue, in the same order)
+  const bool vec = m0 + kDBM <= M && n0 + kDBN <= N && N % 4 == 0 &&
+                   (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+#pragma unroll
+  for (int i = 0; i < kDTM; ++i) {
+    const int rl = wm * kDWM + i * 32 + r;
+    const int64_t row = m0 + rl;
+    const float rs = row_scale[rl];
+    uint16_t* __restrict__ yrow = y + row * N + n0;
+#pragma unroll
+    for (int j = 0; j < kDTN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int cl = wn * kDWN + j * 32 + g * 8 + h * 4;
+        const f32x4 cs = *reinterpret_cast<const f32x4*>(col_scale + cl);
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(col_bias + cl);
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[t] = __builtin_fmaf(acc[i][j][4 * g + t], rs * cs[t], bv[t]);
+          if (epi == 1) v[t] = gelu_erf(v[t]);
+        }
+        const u32x2 pk = {bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+        if (vec) {
+          *reinterpret_cast<u32x2*>(yrow + cl) = pk;
+        } else if (row < M) {
+          const uint16_t hv[4] = {(uint16_t)pk.x, (uint16_t)(pk.x >> 16), (uint16_t)pk.y,
+                                  (uint16_t)(pk.y >> 16)};
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (n0 + cl + t < N) yrow[cl + t] = hv[t];
+        }
+      }
+  }
+}
+
+// Sums the slices of the tail tiles in split order and applies the epilogue
+// of the whole tiles (same operations, same order).  Slices are in the
+// accumulator order of gemm_fp8_dma_kernel; thread q of a tile takes float4 q
+// (4 consecutive columns of one row), so every slice is read contiguously.
+constexpr int kFp8ReduceWgs = 16;             // workgroups per tail tile
+
+__global__ __launch_bounds__(256) void fp8_split_reduce_kernel(
+    const float* __restrict__ part, int64_t main_tiles, int ways, const float* __restrict__ da,
+    const float* __restrict__ dw, const uint16_t* __restrict__ bias, int64_t M, int64_t N, int epi,
+    uint16_t* __restrict__ y) {
+  constexpr int kQuads = kDBM * kDBN / 4;       // float4 per slice
+  constexpr int kPerWg = kQuads / kFp8ReduceWgs;
+  const int64_t tail = blockIdx.x / kFp8ReduceWgs;
+  const int64_t tiles_m = (M + kDBM - 1) / kDBM, tiles_n = (N + kDBN - 1) / kDBN;
+  int64_t tm, tn;
+  grouped_tile(main_tiles + tail, tiles_m, tiles_n, tm, tn);
+  const f32x4* slices = reinterpret_cast<const f32x4*>(part) + tail * ways * (int64_t)kQuads;
+  for (int q = (int)(blockIdx.x % kFp8ReduceWgs) * kPerWg + threadIdx.x;
+       q < (int)(blockIdx.x % kFp8ReduceWgs + 1) * kPerWg; q += 256) {
+    // q = (((wave * 4 + i) * 4 + j) * 64 + lane) * 4 + g
+    const int g = q & 3, lane = (q >> 2) & 63, j = (q >> 8) & 3, i = (q >> 10) & 3, wave = q >> 12;
+    const int rl = (wave >> 1) * kDWM + i * 32 + (lane & 31);
+    const int cl = (wave & 1) * kDWN + j * 32 + g * 8 + (lane >> 5) * 4;
+    const int64_t row = tm * kDBM + rl, col = tn * kDBN + cl;
+    if (row >= M) continue;
+    f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < ways; ++s) sum += slices[s * (int64_t)kQuads + q];
+    const float rs = da[row];
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool ok = col + k < N;
+      const float cs = ok ? dw[col + k] : 0.0f;
+      const float bv = (bias && ok) ? bf16_bits_to_f32(bias[col + k]) : 0.0f;
+      v[k] = __builtin_fmaf(sum[k], rs * cs, bv);
+      if (epi == 1) v[k] = gelu_erf(v[k]);
+    }
+    const uint32_t p01 = bf16x2_rne(v[0], v[1]), p23 = bf16x2_rne(v[2], v[3]);
+    const uint16_t hv[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
+    uint16_t* dst = y + row * N + col;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (col + k < N) dst[k] = hv[k];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fp8_quantize_rowwise(const void* x, int64_t rows, int64_t cols, uint8_t* codes,
@@ -299,12 +597,86 @@ hipError_t launch_fp8_quantize_rowwise(const void* x, int64_t rows, int64_t cols
   return hipGetLastError();
 }
 
+namespace {
+
+// The direct-to-LDS kernel needs K % 128 == 0, 16-byte aligned code rows and
+// operands below 4 GiB; NVFP4_FP8_GEMM_KERNEL=reg pins the register-staged
+// kernel (testing).
+bool use_fp8_dma(int64_t M, int64_t N, int64_t K, uintptr_t align_bits) {
+  if (const char* f = getenv("NVFP4_FP8_GEMM_KERNEL"))
+    if (!strcmp(f, "reg")) return false;
+  const int64_t limit = (int64_t)1 << 32;   // 32-bit source offsets
+  return K % kDBK == 0 && (align_bits & 15) == 0 && M * K < limit && N * K < limit;
+}
+
+struct Fp8SplitPlan {
+  int64_t tiles = 0, main_tiles = 0, tail = 0;
+  int ways = 1;
+  size_t bytes = 0;
+};
+
+// Tail split for the direct-to-LDS kernel: the tiles past the last whole
+// round over the compute units are split into `ways` K ranges of at least
+// kFp8MinSplitStages stages, as many as fill the round, at most kFp8MaxWays
+// (each way adds a slice of partial sums to write and read back).  Below
+// kFp8MinWays the partial-sum traffic costs about what the split saves
+// (measured on the DiT up projection: 96 tail tiles, 2 ways), so the tail is
+// computed whole.  NVFP4_FP8_GEMM_SPLIT=n forces n ways on the tail (testing).
+constexpr int kFp8MinSplitStages = 4;
+constexpr int kFp8MinWays = 3;
+constexpr int kFp8MaxWays = 8;
+
+Fp8SplitPlan plan_fp8_split(int64_t M, int64_t N, int64_t K) {
+  Fp8SplitPlan p;
+  p.tiles = p.main_tiles = ((M + kDBM - 1) / kDBM) * ((N + kDBN - 1) / kDBN);
+  if (p.tiles == 0 || K % kDBK != 0) return p;
+  const int cus = compute_units();
+  const int64_t nk = K / kDBK;
+  const int64_t tail = p.tiles % cus;
+  if (tail == 0) return p;
+  int64_t ways = std::min<int64_t>(std::min<int64_t>(cus / tail, nk / kFp8MinSplitStages),
+                                   kFp8MaxWays);
+  if (ways < kFp8MinWays) ways = 1;
+  if (const char* f = getenv("NVFP4_FP8_GEMM_SPLIT")) ways = std::min<int64_t>(atoi(f), nk);
+  if (ways < 2) return p;
+  p.tail = tail;
+  p.main_tiles = p.tiles - tail;
+  p.ways = (int)ways;
+  p.bytes = (size_t)tail * ways * kDBM * kDBN * sizeof(float);
+  return p;
+}
+
+}  // namespace
+
+size_t gemm_fp8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || !use_fp8_dma(M, N, K, 0)) return 0;
+  return plan_fp8_split(M, N, K).bytes;
+}
+
 hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_codes,
                            const float* w_scales, const void* bias, int64_t M, int64_t N,
-                           int64_t K, int epilogue, void* y, hipStream_t stream) {
+                           int64_t K, int epilogue, void* y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const uintptr_t al = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(w_codes);
+  if (use_fp8_dma(M, N, K, al)) {
+    const Fp8SplitPlan plan = plan_fp8_split(M, N, K);
+    const bool split = plan.ways > 1 && workspace && workspace_bytes >= plan.bytes;
+    const SplitK sk = split ? SplitK{static_cast<float*>(workspace), plan.main_tiles, plan.ways}
+                            : SplitK{nullptr, plan.tiles, 1};
+    const int64_t grid = split ? plan.main_tiles + plan.tail * plan.ways : plan.tiles;
+    const uint16_t* b16 = reinterpret_cast<const uint16_t*>(bias);
+    uint16_t* y16 = reinterpret_cast<uint16_t*>(y);
+    hipLaunchKernelGGL(gemm_fp8_dma_kernel, dim3((unsigned)grid), dim3(kDNT), 0, stream, a_codes,
+                       a_scales, w_codes, w_scales, b16, M, N, K, epilogue, y16, sk);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !split) return e;
+    hipLaunchKernelGGL(fp8_split_reduce_kernel, dim3((unsigned)(plan.tail * kFp8ReduceWgs)),
+                       dim3(256), 0, stream, static_cast<const float*>(workspace), plan.main_tiles,
+                       plan.ways, a_scales, w_scales, b16, M, N, epilogue, y16);
+    return hipGetLastError();
+  }
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   hipLaunchKernelGGL(gemm_fp8_kernel, dim3((unsigned)tiles), dim3(kNT), 0, stream, a_codes, a_scales,
                      w_codes, w_scales, reinterpret_cast<const uint16_t*>(bias), M, N, K, epilogue,
                      reinterpret_cast<uint16_t*>(y), (al & 15) == 0 ? 1 : 0);

@@ -639,30 +639,8 @@ __device__ __forceinline__ void main_loop3(const Operand& A, const Operand& Wt, 
 // idle.  Its tiles are then each split into `ways` ranges of K stages given to
 // different workgroups, which store their fp32 partial sums, row-major, in
 // their own slice of the workspace; a second kernel adds the slices in split
-// order (the result does not depend on timing) and applies the epilogue.
-struct SplitK {
-  float* part;         // [tail tiles][ways][BM][BN] fp32 partial sums
-  int64_t main_tiles;  // tiles computed whole, by workgroups 0 .. main_tiles-1
-  int ways;            // K ranges per tail tile (1: no split)
-};
-
-// Work of this workgroup: tile (tm, tn), and for a tail tile its index among
-// the tail tiles and its split (split < 0 for a whole tile).
-__device__ __forceinline__ void split_coords(int64_t tiles_m, int64_t tiles_n, const SplitK& sk,
-                                             int64_t& tm, int64_t& tn, int64_t& tail,
-                                             int& split) {
-  const int64_t b = blockIdx.x;
-  if (b < sk.main_tiles) {
-    grouped_tile(xcd_order(b, sk.main_tiles), tiles_m, tiles_n, tm, tn);
-    tail = -1;
-    split = -1;
-  } else {
-    const int64_t u = b - sk.main_tiles;
-    tail = u / sk.ways;
-    split = (int)(u - tail * sk.ways);
-    grouped_tile(sk.main_tiles + tail, tiles_m, tiles_n, tm, tn);
-  }
-}
+// order (the result does not depend on timing) and applies the epilogue
+// (SplitK and split_coords describe the assignment).
 
 // This workgroup's partial sums into its slice, at their tile positions (the
 // accumulator layout of the epilogue).
@@ -814,14 +792,6 @@ bool use_pipe(int64_t M, int64_t N) {
   return M * N > (int64_t)256 * 256 * 128;
 }
 
-int compute_units() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
-  return n;
-}
-
 struct SplitPlan {
   int64_t tiles = 0;        // all tiles
   int64_t main_tiles = 0;   // tiles computed whole
@@ -886,6 +856,14 @@ hipError_t launch_pipe(const uint8_t* a_codes, const uint8_t* a_scales, const fl
 }
 
 }  // namespace
+
+int compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
 
 size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || !use_pipe(M, N)) return 0;

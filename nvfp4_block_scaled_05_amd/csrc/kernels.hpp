@@ -6,6 +6,9 @@
 
 namespace nvfp4 {
 
+// Compute units of the current device (256 if the query fails).
+int compute_units();
+
 // Upper bound on the partial maxima the amax pass writes (workspace words).
 static constexpr int kMaxAmaxPartials = 1024;
 
@@ -45,7 +48,10 @@ hipError_t launch_fp8_quantize_rowwise(const void* x, int64_t rows, int64_t cols
                                        float* row_scales, int32_t* dev_status, hipStream_t stream);
 hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_codes,
                            const float* w_scales, const void* bias, int64_t M, int64_t N,
-                           int64_t K, int epilogue, void* y, hipStream_t stream);
+                           int64_t K, int epilogue, void* y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+// Workspace bytes launch_gemm_fp8 can use to split the tail tiles over K.
+size_t gemm_fp8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, int64_t M, int64_t N,
                             int64_t K, int epilogue, void* y, hipStream_t stream);

@@ -34,14 +34,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
         assert n in _binding.SIGNATURES, n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.nvfp4_abi_version() == 4
+    assert lib.nvfp4_abi_version() == 5
     for code in range(-8, 1):
         assert lib.nvfp4_status_string(code)
     assert lib.nvfp4_status_string(-99) == b"unknown status"
@@ -149,11 +149,28 @@ def test_fp8_argument_errors(lib):
     assert fq(A + 8, 4, 32, A, A, None, None) == ALIGN
     assert fq(A, 4, 32, A + 4, A, None, None) == ALIGN
     fg = lib.nvfp4_fp8_gemm
-    assert fg(A, A, A, A, None, 8, 8, 64, 0, None, None) == NULL
-    assert fg(A, A, A, A, None, 8, 8, 40, 0, A, None) == SHAPE
-    assert fg(A + 8, A, A, A, None, 8, 8, 64, 0, A, None) == ALIGN
-    assert fg(A, A, A, A, None, 8, 8, 64, 9, A, None) == ARG
-    assert fg(A, A, A, A, None, 8, 8, 64, 0, A, None) in (OK, DEVICE)
+
+    def f(M=8, N=8, K=64, epi=0, y=A, ac=A, ws=None, wsb=0):
+        return fg(ac, A, A, A, None, M, N, K, epi, y, ws, wsb, None)
+    assert f(y=None) == NULL
+    assert f(K=40) == SHAPE
+    assert f(ac=A + 8) == ALIGN
+    assert f(ws=A + 64, wsb=1 << 20) == ALIGN
+    assert f(epi=9) == ARG
+    assert f() in (OK, DEVICE)
+
+
+def test_fp8_gemm_workspace_bytes(lib):
+    wb = lib.nvfp4_fp8_gemm_workspace_bytes
+    assert wb(0, 64, 128) == wb(-1, 64, 128) == wb(64, 64, 48) == 0
+    # K % 128 != 0 runs the register-staged kernel, which never splits
+    assert wb(16896, 3072, 12288 + 64) == 0
+    # MLP down at 2048^2 with a CFG pair: 792 tiles of 256x256, 24 past three
+    # rounds over 256 compute units, split 8 ways (at most 8; 10 would fit)
+    assert wb(16896, 3072, 12288) == 24 * 8 * 256 * 256 * 4
+    # MLP up: 96 tiles past 12 rounds would split only 2 ways: whole
+    assert wb(16896, 12288, 3072) == 0
+    assert wb(256 * 16, 256 * 16, 4096) == 0        # whole rounds only
 
 
 def test_layer_predicate_matches_python_re(lib):

@@ -83,9 +83,18 @@ def _close(y, ref, label):
     assert float((ulp_diff(y, ref) > 1).mean()) <= 1e-2, label
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (130, 70, 48), (300, 257, 1088), (200, 300, 3088),
-                                   (1, 129, 16), (513, 256, 512)])
-def test_fp8_gemm_small_and_ragged(M, N, K):
+# K % 128 == 0 runs the direct-to-LDS kernel (1, 2, 3, 4, 9, 10 stages of 128,
+# ragged M and N); other K the register-staged one.  "reg" pins the latter.
+GEMM_SHAPES = [(64, 64, 64), (130, 70, 48), (300, 257, 1088), (200, 300, 3088), (1, 129, 16),
+               (513, 256, 512), (1, 1, 128), (256, 256, 256), (257, 513, 384),
+               (300, 257, 1152), (70, 600, 1280)]
+
+
+@pytest.mark.parametrize("kernel", ["default", "reg"])
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_fp8_gemm_small_and_ragged(M, N, K, kernel, monkeypatch):
+    if kernel == "reg":
+        monkeypatch.setenv("NVFP4_FP8_GEMM_KERNEL", "reg")
     a_bits = W.random_matrix(M + K, (M, K), "t3")
     w_bits = W.random_matrix(N + K, (N, K), "normal", 0.02)
     b_bits = W.random_matrix(M + N, (1, N), "normal", 0.1)[0]
@@ -106,3 +115,40 @@ def test_fp8_gemm_mlp_up_sampled_rows():
     rows = np.unique(np.concatenate([[0, 16895], np.random.default_rng(0).choice(16896, 40, replace=False)]))
     ref, _ = gemm_fp8_exact_rows(rx, rw, rows, gelu=True)
     _close(y[rows], ref, "fp8 up sampled rows")
+
+
+def test_fp8_gemm_mlp_down_sampled_rows():
+    # the MLP down projection at 2048^2: W_down [3072,12288] against a seeded
+    # N(0, 0.5) stand-in for the hidden activation H [16896,12288]
+    d = W.mlp_2048()
+    rng = np.random.default_rng(1)
+    h_bits = W.random_matrix(77, (16896, 12288), "normal", 0.5)
+    qh, rh = check_fp8_quantize(h_bits, "H")
+    qw, rw = check_fp8_quantize(d["w_down"], "W_down")
+    b_bits = W.random_matrix(78, (1, 3072), "normal", 0.1)[0]
+    y = bits_of(nv.fp8_gemm(qh, qw, bias=to_dev(b_bits)))
+    rows = np.unique(np.concatenate([[0, 16895], rng.choice(16896, 24, replace=False)]))
+    ref, _ = gemm_fp8_exact_rows(rh, rw, rows, bias_bits=b_bits)
+    _close(y[rows], ref, "fp8 down sampled rows")
+
+
+@pytest.mark.parametrize("ways", [2, 3, 7])
+@pytest.mark.parametrize("M,N,K", [(600, 520, 1280), (257, 300, 2048)])
+def test_fp8_gemm_split_k(M, N, K, ways, monkeypatch):
+    # the tail tiles split over K (forced), partial sums added in split order
+    monkeypatch.setenv("NVFP4_FP8_GEMM_SPLIT", str(ways))
+    a_bits = W.random_matrix(M * 3 + K, (M, K), "t3")
+    w_bits = W.random_matrix(N * 3 + K, (N, K), "normal", 0.02)
+    b_bits = W.random_matrix(M + N + 5, (1, N), "normal", 0.1)[0]
+    qa, ra = check_fp8_quantize(a_bits, "A")
+    qw, rw = check_fp8_quantize(w_bits, "W")
+    ws = nv.fp8_gemm_workspace(M, N, K)
+    assert ws is not None
+    for epi in ("none", "gelu"):
+        y1 = bits_of(nv.fp8_gemm(qa, qw, bias=to_dev(b_bits), epilogue=epi, workspace=ws))
+        y2 = bits_of(nv.fp8_gemm(qa, qw, bias=to_dev(b_bits), epilogue=epi, workspace=ws))
+        assert np.array_equal(y1, y2), "split result depends on timing"
+        ref, _ = gemm_fp8_fp64(ra, rw, bias_bits=b_bits, gelu=epi == "gelu")
+        _close(y1, ref, f"fp8 split {ways} {M}x{N}x{K} {epi}")
+        y0 = bits_of(nv.fp8_gemm(qa, qw, bias=to_dev(b_bits), epilogue=epi, workspace=None))
+        _close(y0, ref, f"fp8 whole tiles {M}x{N}x{K} {epi}")
