@@ -760,6 +760,528 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_pipe_kernel(
   finish_tile<C>(acc, (*sa) * (*sw), bias, epi, M, N, m0, n0, out, lds);
 }
 
+// ---------------------------------------------------------------------------
+// v5: direct-to-LDS operands, both decoded in registers.  For K % 128 == 0.
+// Workgroup of 4 waves in 2x2 over a 256x256 tile, each wave 128x128 (4x4
+// MFMA tiles, 256 fp32 accumulators per lane).  K advances 128 per stage
+// (eight 16-K MFMA steps), triple-buffered in LDS; a stage holds per row 64
+// bytes of codes and 8 block-scale bytes of each operand (36 KB).
+//   * Codes and scales go from global memory straight into LDS (the gfx950
+//     global->LDS load: one instruction fills 1 KB with 16-byte pieces, or
+//     256 B with 4-byte ones, lane L's at offset L times the size).  Inside a
+//     64-byte code row the 16-byte pieces are permuted by an XOR with
+//     (row / 4) % 4, which makes the fragment reads (16 lanes, 16 consecutive
+//     rows, one logical piece) hit 16 different bank groups.
+//   * Same K permutation as v1-v3 at this width: lanes 0-31 of a wave take
+//     elements 0-63 of the stage, lanes 32-63 elements 64-127; MFMA step s
+//     takes code word s of each lane's 32 bytes, so A and W agree on k.
+//   * Each wave decodes its own 128 rows of A and 128 rows of W from the
+//     packed codes (no fp16 copy in LDS): LDS traffic is the codes only.
+//   * Three stage slots in LDS (108 KB): the loads of stage t+2 are issued
+//     during stage t, after its packed operands have all been read into
+//     registers, so no LDS read waits on a load in flight.
+//   * The decode of step s+1 is interleaved with the MFMAs of step s; the
+//     MFMAs of a stage's last step run after the next barrier, while the next
+//     stage's LDS reads are in flight.
+//   * The weight fragment is the MFMA's first operand, so acc[i][j] holds the
+//     transposed tile: lane (r, h) has row m = i*32 + r and the four
+//     consecutive columns n = j*32 + 8g + 4h + t at elements 4g + t.
+// Rows past M or N are read clamped to the last row; their results are never
+// stored.
+// ---------------------------------------------------------------------------
+constexpr int kVBM = 256, kVBN = 256, kVBK = 128, kVNT = 256;
+constexpr int kVWM = 128, kVWN = 128, kVTM = 4, kVTN = 4;
+constexpr int kVCodeRow = kVBK / 2;                 // 64 code bytes per row and stage
+constexpr int kVScaleRow = kVBK / 16;               // 8 scale bytes per row and stage
+constexpr int kVA = 0;                              // A codes
+constexpr int kVW = kVA + kVBM * kVCodeRow;         // W codes
+constexpr int kVSA = kVW + kVBN * kVCodeRow;        // A scales
+constexpr int kVSW = kVSA + kVBM * kVScaleRow;      // W scales
+constexpr int kVStage = kVSW + kVBN * kVScaleRow;   // 36 KB
+
+// This lane's source offsets (bytes from the start of the operand's codes /
+// scales; rows * K / 2 < 2^32 is checked on the host).
+struct V5Src {
+  uint32_t ac[4], wc[4];     // code chunks of 16 rows
+  uint32_t as[2], ws[2];     // scale chunks of 32 rows
+};
+
+__device__ __forceinline__ void v5_setup(int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                         V5Src& d) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t cpitch = K / 2, spitch = K / 16;
+  const int piece = (lane & 3) ^ ((lane >> 4) & 3);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * (wave * 4 + i) + (lane >> 2);
+    const int64_t ra = m0 + row < M ? m0 + row : M - 1;
+    const int64_t rw = n0 + row < N ? n0 + row : N - 1;
+    d.ac[i] = (uint32_t)(ra * cpitch + piece * 16);
+    d.wc[i] = (uint32_t)(rw * cpitch + piece * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 32 * (wave * 2 + i) + (lane >> 1);
+    const int64_t ra = m0 + row < M ? m0 + row : M - 1;
+    const int64_t rw = n0 + row < N ? n0 + row : N - 1;
+    d.as[i] = (uint32_t)(ra * spitch + (lane & 1) * 4);
+    d.ws[i] = (uint32_t)(rw * spitch + (lane & 1) * 4);
+  }
+}
+
+__device__ __forceinline__ void v5_issue(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+                                         const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+                                         const V5Src& d, int kt, uint8_t* stage) {
+  const int wave = threadIdx.x >> 6;
+  const uint8_t* ack = ac + (int64_t)kt * kVCodeRow;
+  const uint8_t* wck = wc + (int64_t)kt * kVCodeRow;
+  const uint8_t* ask = as + (int64_t)kt * kVScaleRow;
+  const uint8_t* wsk = ws + (int64_t)kt * kVScaleRow;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = wave * 4 + i;
+    __builtin_amdgcn_global_load_lds(ack + d.ac[i], stage + kVA + c * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wck + d.wc[i], stage + kVW + c * 1024, 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = wave * 2 + i;
+    __builtin_amdgcn_global_load_lds(ask + d.as[i], stage + kVSA + c * 256, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(wsk + d.ws[i], stage + kVSW + c * 256, 4, 0, 0);
+  }
+}
+
+// One lane's packed operands for a stage: tiles 0-3 are A (i), 4-7 are W (j).
+struct V5Packed {
+  u32x4 lo[8], hi[8];   // code words 0-3 and 4-7 (MFMA steps)
+  f16x2 s01[8], s23[8]; // block scales (4 blocks) as fp16
+};
+
+struct V5Ops {
+  f16x8 v[8];
+};
+
+__device__ __forceinline__ void v5_read(const uint8_t* stage, int a_row, int w_row, int h, int x,
+                                        V5Packed& p, uint32_t (&sc)[8]) {
+  const int p0 = ((2 * h) ^ x) << 4, p1 = ((2 * h + 1) ^ x) << 4;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int row = (t < 4 ? a_row + t * 32 : w_row + (t - 4) * 32);
+    const uint8_t* cr = stage + (t < 4 ? kVA : kVW) + row * kVCodeRow;
+    p.lo[t] = *reinterpret_cast<const u32x4*>(cr + p0);
+    p.hi[t] = *reinterpret_cast<const u32x4*>(cr + p1);
+    sc[t] = *reinterpret_cast<const uint32_t*>(stage + (t < 4 ? kVSA : kVSW) + row * kVScaleRow + h * 4);
+  }
+}
+
+__device__ __forceinline__ void v5_scales(const uint32_t (&sc)[8], V5Packed& p) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    p.s01[t] = e4m3_pair_to_f16x2<false>(sc[t]);
+    p.s23[t] = e4m3_pair_to_f16x2<true>(sc[t]);
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void v5_decode(const V5Packed& p, V5Ops& o) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t w = S < 4 ? p.lo[t][S & 3] : p.hi[t][S & 3];
+    const _Float16 s = (S >> 1) == 0 ? p.s01[t].x : (S >> 1) == 1 ? p.s01[t].y
+                     : (S >> 1) == 2 ? p.s23[t].x : p.s23[t].y;
+    o.v[t] = decode8(w, s);
+  }
+}
+
+__device__ __forceinline__ void v5_mfma(const V5Ops& o, f32x16 (&acc)[kVTM][kVTN]) {
+#pragma unroll
+  for (int i = 0; i < kVTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kVTN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.v[4 + j], o.v[i], acc[i][j], 0, 0, 0);
+}
+
+// MFMAs of step S-1 (in `cur`) interleaved with the decode of step S (into `nxt`).
+template <int S>
+__device__ __forceinline__ void v5_step(const V5Packed& p, const V5Ops& cur, V5Ops& nxt,
+                                        f32x16 (&acc)[kVTM][kVTN]) {
+  v5_decode<S>(p, nxt);
+  v5_mfma(cur, acc);
+#pragma unroll
+  for (int m = 0; m < kVTM * kVTN; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU (decode)
+  }
+}
+
+// Steps 1-7 of a stage whose step-0 operands are in `o0`; leaves step 7's in `o1`.
+__device__ __forceinline__ void v5_steps(const V5Packed& p, V5Ops& o0, V5Ops& o1,
+                                         f32x16 (&acc)[kVTM][kVTN]) {
+  v5_step<1>(p, o0, o1, acc);
+  v5_step<2>(p, o1, o0, acc);
+  v5_step<3>(p, o0, o1, acc);
+  v5_step<4>(p, o1, o0, acc);
+  v5_step<5>(p, o0, o1, acc);
+  v5_step<6>(p, o1, o0, acc);
+  v5_step<7>(p, o0, o1, acc);
+}
+
+// Stage data in LDS: this wave's loads for it have landed (vmcnt; with
+// `next_in_flight` the 12 loads issued since -- the following stage's -- may
+// still be outstanding; they complete in order), then the workgroup barrier
+// makes every wave's loads visible and ends every read of the slot about to
+// be refilled.
+// (__syncthreads() would add a release fence, which waits for every load in
+// flight; the waits here are explicit, and the asm barrier with a memory
+// clobber keeps the compiler from moving memory accesses across it.)
+__device__ __forceinline__ void v5_barrier(bool next_in_flight) {
+  if (next_in_flight)
+    __builtin_amdgcn_s_waitcnt(0x007C);   // vmcnt(12) lgkmcnt(0)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// One stage after the first, from slot `cur`: read all of its packed operands
+// (so no LDS read follows the loads issued below), run the previous stage's
+// last MFMAs while the reads are in flight, issue the loads of the stage two
+// ahead into `refill`, then this stage's steps.
+__device__ __forceinline__ void v5_stage(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+                                         const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+                                         const V5Src& src, const uint8_t* cur, uint8_t* refill,
+                                         bool next_in_flight, bool do_refill, int k_refill, int a_row,
+                                         int w_row, int h, int x, V5Packed& p, V5Ops& o0, V5Ops& o1,
+                                         f32x16 (&acc)[kVTM][kVTN]) {
+  v5_barrier(next_in_flight);
+  uint32_t sc[8];
+  v5_read(cur, a_row, w_row, h, x, p, sc);
+  v5_mfma(o1, acc);                        // previous stage, step 7
+#pragma unroll
+  for (int m = 0; m < kVTM * kVTN; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+  }
+  if (do_refill) v5_issue(ac, as, wc, ws, src, k_refill, refill);
+  v5_scales(sc, p);
+  v5_decode<0>(p, o0);
+  v5_steps(p, o0, o1, acc);
+}
+
+// Epilogue of v5: acc * sA*sW + bias (one fused multiply-add), optional GELU,
+// bf16 round-to-nearest-even, optional max |bf16 y| (one atomic per
+// workgroup) -- the operations of epilogue(), in the same order.
+// Fully unrolled over 256 accumulators per lane this is ~100 KB of code, more
+// than the instruction cache holds; instead each wave moves 32 rows of its
+// accumulators at a time into its own 16 KB of LDS (fp32, 16-byte chunks of a
+// 512-byte row permuted by XOR with the row, conflict-free both ways) and a
+// short loop takes them back 4 consecutive columns per lane: 32 lanes cover
+// a 128-column row segment, so the 8-byte stores complete whole lines.
+template <int EPI>
+__device__ __forceinline__ float v5_finish(float a, float scale, float b) {
+  const float v = __builtin_fmaf(a, scale, b);
+  return EPI == 1 ? gelu_erf(v) : v;
+}
+
+template <int EPI>
+__device__ __forceinline__ float v5_slice_out(const float* st, float scale, f32x4 bv, int64_t row0,
+                                              int64_t col, int64_t M, int64_t N, bool vec,
+                                              uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63, c = lane & 31;
+  float amax = 0.0f;
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int rr = it * 2 + (lane >> 5);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(st + rr * 128 + ((c ^ rr) << 2));
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = v5_finish<EPI>(a[t], scale, bv[t]);
+    const u32x2 pk = {bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+    const int64_t row = row0 + rr;
+    if (vec) {
+      *reinterpret_cast<u32x2*>(y + row * N + col) = pk;
+      amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                                                   __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]))));
+    } else if (row < M) {
+      const uint16_t hv[4] = {(uint16_t)pk.x, (uint16_t)(pk.x >> 16), (uint16_t)pk.y, (uint16_t)(pk.y >> 16)};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (col + t < N) {
+          y[row * N + col + t] = hv[t];
+          amax = __builtin_fmaxf(amax, __builtin_fabsf(v[t]));
+        }
+    }
+  }
+  return amax;
+}
+
+__device__ __forceinline__ void v5_epilogue(const f32x16 (&acc)[kVTM][kVTN], float scale,
+                                            const float* col_bias, int epi, int64_t M, int64_t N,
+                                            int64_t m0, int64_t n0, uint16_t* __restrict__ y,
+                                            uint32_t* __restrict__ y_amax, float* st) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r = lane & 31, h = lane >> 5;
+  const bool vec = m0 + kVBM <= M && n0 + kVBN <= N && N % 4 == 0 &&
+                   (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+  const int cl = wn * kVWN + (lane & 31) * 4;               // this lane's 4 columns when reading back
+  const f32x4 bv = *reinterpret_cast<const f32x4*>(col_bias + cl);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kVTM; ++i) {
+    // rows i*32 .. i*32+31 of the wave's tile: lane (r, h) holds row r, and
+    // 4 consecutive columns j*32 + 8g + 4h at elements 4g .. 4g+3
+#pragma unroll
+    for (int j = 0; j < kVTN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = j * 8 + g * 2 + h;                    // 16-byte chunk of the 512-byte row
+        *reinterpret_cast<f32x4*>(st + r * 128 + ((c ^ r) << 2)) =
+            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0): the wave's writes landed
+    __builtin_amdgcn_wave_barrier();
+    const int64_t row0 = m0 + wm * kVWM + i * 32;
+    const float a = epi == 1 ? v5_slice_out<1>(st, scale, bv, row0, n0 + cl, M, N, vec, y)
+                             : v5_slice_out<0>(st, scale, bv, row0, n0 + cl, M, N, vec, y);
+    amax = __builtin_fmaxf(amax, a);
+    __builtin_amdgcn_s_waitcnt(0xC07F);                     // reads done before the next slice's writes
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (y_amax) {   // one atomic per workgroup
+    __shared__ uint32_t wave_amax[kVNT / 64];
+    uint32_t a = (bf16x2_rne(amax, 0.0f) & 0xFFFFu) << 16;
+    a = wave_max_u32(a);
+    if (lane == 0) wave_amax[wave] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int w = 0; w < kVNT / 64; ++w) m = max(m, wave_amax[w]);
+      atomicMax(y_amax, m);
+    }
+  }
+}
+
+// NVFP4 output of v5 under the static tensor scale derived from
+// *out.amax_static: the bf16 values of v5_slice_out (same operations) are
+// staged in the wave's LDS, 32 rows x 128 columns at a time, and every lane
+// then quantizes whole 16-element blocks with the quantizer's own routine --
+// the bytes nvfp4_quantize writes for the bf16 output.  N % 16 == 0.
+template <int EPI>
+__device__ __forceinline__ void v5_slice_quant(const float* st, uint16_t* st16, float scale, f32x4 bv,
+                                               int64_t row0, int64_t col_w, int64_t M, int64_t N,
+                                               bool degenerate, float s_enc, float s_dec,
+                                               const Out& out) {
+  const int lane = threadIdx.x & 63, c = lane & 31;
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int rr = it * 2 + (lane >> 5);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(st + rr * 128 + ((c ^ rr) << 2));
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = v5_finish<EPI>(a[t], scale, bv[t]);
+    *reinterpret_cast<u32x2*>(st16 + rr * 136 + c * 4) = u32x2{bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);                       // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  const int64_t code_pitch = N / 2, scale_pitch = N / 16;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int b = lane + 64 * k, rr = b >> 3, blk = b & 7;   // 32 rows x 8 blocks
+    const int64_t row = row0 + rr, col = col_w + blk * 16;
+    const u32x4* src = reinterpret_cast<const u32x4*>(st16 + rr * 136 + blk * 16);
+    u32x2 cw;
+    uint32_t S;
+    quantize_block(src[0], src[1], degenerate, s_enc, s_dec, cw, S);
+    if (row < M && col < N) {
+      *reinterpret_cast<u32x2*>(out.codes + row * code_pitch + col / 2) = cw;
+      out.scales[row * scale_pitch + col / 16] = (uint8_t)S;
+    }
+  }
+}
+
+__device__ __forceinline__ void v5_epilogue_quant(const f32x16 (&acc)[kVTM][kVTN], float scale,
+                                                  const float* col_bias, int epi, int64_t M,
+                                                  int64_t N, int64_t m0, int64_t n0, const Out& out,
+                                                  float* st, uint16_t* st16) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r = lane & 31, h = lane >> 5;
+  // tensor scales as the quantizer derives them from a given amax
+  const uint32_t amax_bits = __float_as_uint(*out.amax_static) & 0x7FFFFFFFu;
+  if (amax_bits >= 0x7F800000u) {                  // Inf / NaN amax: no scale exists
+    if (blockIdx.x == 0 && threadIdx.x == 0) *out.tensor_scale = __uint_as_float(0x7FC00000u);
+    return;
+  }
+  bool degenerate;
+  float s_enc, s_dec;
+  tensor_scales(__uint_as_float(amax_bits), degenerate, s_enc, s_dec);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *out.tensor_scale = s_dec;
+  const f32x4 bv = *reinterpret_cast<const f32x4*>(col_bias + wn * kVWN + (lane & 31) * 4);
+#pragma unroll
+  for (int i = 0; i < kVTM; ++i) {
+#pragma unroll
+    for (int j = 0; j < kVTN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = j * 8 + g * 2 + h;
+        *reinterpret_cast<f32x4*>(st + r * 128 + ((c ^ r) << 2)) =
+            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    const int64_t row0 = m0 + wm * kVWM + i * 32, col_w = n0 + wn * kVWN;
+    if (epi == 1)
+      v5_slice_quant<1>(st, st16, scale, bv, row0, col_w, M, N, degenerate, s_enc, s_dec, out);
+    else
+      v5_slice_quant<0>(st, st16, scale, bv, row0, col_w, M, N, degenerate, s_enc, s_dec, out);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// kQuant: NVFP4 output (out.codes, out.scales, out.tensor_scale) instead of
+// bf16 (out.y, out.y_amax); whole tiles only.
+template <bool kQuant>
+__global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ sa, const uint8_t* __restrict__ w_codes,
+    const uint8_t* __restrict__ w_scales, const float* __restrict__ sw,
+    const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi, Out out,
+    SplitK sk) {
+  // three stage slots: the loads of stage t + 2 are issued while stage t runs
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * kVStage];
+  __shared__ __attribute__((aligned(16))) float col_bias[kVBN];
+  const int64_t tiles_m = (M + kVBM - 1) / kVBM, tiles_n = (N + kVBN - 1) / kVBN;
+  int64_t tm, tn, tail;
+  int split;
+  split_coords(tiles_m, tiles_n, sk, tm, tn, tail, split);
+  const int64_t m0 = tm * kVBM, n0 = tn * kVBN;
+  {
+    const int64_t c = n0 + threadIdx.x;
+    col_bias[threadIdx.x] = (bias && c < N) ? bf16_bits_to_f32(bias[c]) : 0.0f;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, h = lane >> 5, x = (r >> 2) & 3;
+  const int a_row = wm * kVWM + r, w_row = wn * kVWN + r;
+
+  V5Src src;
+  v5_setup(M, N, K, m0, n0, src);
+  f32x16 acc[kVTM][kVTN];
+#pragma unroll
+  for (int i = 0; i < kVTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kVTN; ++j) acc[i][j] = f32x16{};
+
+  // stages [kb, ke) of 128 K: all of them, or this split's share
+  const int nk = (int)(K / kVBK);
+  const int kb = split < 0 ? 0 : (int)((int64_t)split * nk / sk.ways);
+  const int ke = split < 0 ? nk : (int)((int64_t)(split + 1) * nk / sk.ways);
+  const int ns = ke - kb;
+  V5Packed p;
+  V5Ops o0, o1;
+  // stage kb + t lives in slot t % 3
+  v5_issue(a_codes, a_scales, w_codes, w_scales, src, kb, lds);
+  if (ns > 1) v5_issue(a_codes, a_scales, w_codes, w_scales, src, kb + 1, lds + kVStage);
+  v5_barrier(ns > 1);
+  {
+    uint32_t sc[8];
+    v5_read(lds, a_row, w_row, h, x, p, sc);
+    if (ns > 2) v5_issue(a_codes, a_scales, w_codes, w_scales, src, kb + 2, lds + 2 * kVStage);
+    v5_scales(sc, p);
+  }
+  v5_decode<0>(p, o0);
+  v5_steps(p, o0, o1, acc);
+  for (int t = 1; t < ns; ++t) {
+    const int slot = t % 3, rslot = (t + 2) % 3;
+    v5_stage(a_codes, a_scales, w_codes, w_scales, src, lds + slot * kVStage, lds + rslot * kVStage,
+             t + 1 < ns, t + 2 < ns, kb + t + 2, a_row, w_row, h, x, p, o0, o1, acc);
+  }
+  v5_mfma(o1, acc);
+
+  if (!kQuant && split >= 0) {
+    // a tail split: fp32 partial sums into its slice in accumulator order --
+    // float4 number (((wave * 4 + i) * 4 + j) * 64 + lane) * 4 + g holds
+    // acc[i][j][4g .. 4g+3], so each wave writes 4 KB contiguous per tile
+    f32x4* slice = reinterpret_cast<f32x4*>(sk.part + (tail * sk.ways + split) * (int64_t)(kVBM * kVBN));
+#pragma unroll
+    for (int i = 0; i < kVTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kVTN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          slice[(((wave * kVTM + i) * kVTN + j) * 64 + lane) * 4 + g] =
+              f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    return;
+  }
+  __syncthreads();   // every wave is done with the stage buffers
+  float* st = reinterpret_cast<float*>(lds + wave * 16384);
+  if (kQuant)   // bf16 staging after the four fp32 areas: 32 rows of 136 halves per wave
+    v5_epilogue_quant(acc, (*sa) * (*sw), col_bias, epi, M, N, m0, n0, out, st,
+                      reinterpret_cast<uint16_t*>(lds + 4 * 16384 + wave * 32 * 136 * 2));
+  else
+    v5_epilogue(acc, (*sa) * (*sw), col_bias, epi, M, N, m0, n0, out.y, out.y_amax, st);
+}
+
+// Sums the slices of v5's tail tiles in split order and applies v5's epilogue
+// (same operations, same order).  Slices are in v5's accumulator order;
+// thread q of a tile takes float4 q (4 consecutive columns of one row), so
+// every slice is read contiguously.  The output amax is reduced in the
+// workgroup first: one atomic per workgroup.
+constexpr int kV5ReduceWgs = 16;            // workgroups per tail tile
+
+__global__ __launch_bounds__(256) void v5_split_reduce_kernel(
+    const float* __restrict__ part, int64_t main_tiles, int ways, const float* __restrict__ sa,
+    const float* __restrict__ sw, const uint16_t* __restrict__ bias, int64_t M, int64_t N,
+    int epi, uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax) {
+  constexpr int kQuads = kVBM * kVBN / 4;
+  constexpr int kPerWg = kQuads / kV5ReduceWgs;
+  const int64_t tail = blockIdx.x / kV5ReduceWgs;
+  const int64_t tiles_m = (M + kVBM - 1) / kVBM, tiles_n = (N + kVBN - 1) / kVBN;
+  int64_t tm, tn;
+  grouped_tile(main_tiles + tail, tiles_m, tiles_n, tm, tn);
+  const float scale = (*sa) * (*sw);
+  const f32x4* slices = reinterpret_cast<const f32x4*>(part) + tail * ways * (int64_t)kQuads;
+  float amax = 0.0f;
+  for (int q = (int)(blockIdx.x % kV5ReduceWgs) * kPerWg + threadIdx.x;
+       q < (int)(blockIdx.x % kV5ReduceWgs + 1) * kPerWg; q += 256) {
+    // q = (((wave * 4 + i) * 4 + j) * 64 + lane) * 4 + g
+    const int g = q & 3, lane = (q >> 2) & 63, j = (q >> 8) & 3, i = (q >> 10) & 3, wave = q >> 12;
+    const int rl = (wave >> 1) * kVWM + i * 32 + (lane & 31);
+    const int cl = (wave & 1) * kVWN + j * 32 + g * 8 + (lane >> 5) * 4;
+    const int64_t row = tm * kVBM + rl, col = tn * kVBN + cl;
+    if (row >= M) continue;
+    f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < ways; ++s) sum += slices[s * (int64_t)kQuads + q];
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float bv = (bias && col + k < N) ? bf16_bits_to_f32(bias[col + k]) : 0.0f;
+      v[k] = __builtin_fmaf(sum[k], scale, bv);
+      if (epi == 1) v[k] = gelu_erf(v[k]);
+    }
+    const uint32_t p01 = bf16x2_rne(v[0], v[1]), p23 = bf16x2_rne(v[2], v[3]);
+    const uint16_t hv[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
+    uint16_t* dst = y + row * N + col;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (col + k < N) {
+        dst[k] = hv[k];
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(v[k]));
+      }
+  }
+  if (y_amax) {
+    __shared__ uint32_t wave_amax[4];
+    uint32_t a = (bf16x2_rne(amax, 0.0f) & 0xFFFFu) << 16;
+    a = wave_max_u32(a);
+    if ((threadIdx.x & 63) == 0) wave_amax[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t m = max(max(wave_amax[0], wave_amax[1]), max(wave_amax[2], wave_amax[3]));
+      atomicMax(y_amax, m);
+    }
+  }
+}
+
 __global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
 
 template <class C>
@@ -782,14 +1304,25 @@ hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const fl
 using CfgPipe = Cfg<256, 256, 4, 2, 1>;    // 8 waves of 64x128 (v3)
 using CfgSmall = Cfg<128, 128, 2, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU (v1)
 
-// DiT-sized problems run v3 on 256x256 tiles; small ones v1 on 128x128 tiles,
-// two workgroups per CU.  NVFP4_GEMM_KERNEL=small|pipe pins one (testing).
+// DiT-sized problems run v5 (K % 128 == 0, aligned rows) or v3 on 256x256
+// tiles; small ones v1 on 128x128 tiles, two workgroups per CU.
+// NVFP4_GEMM_KERNEL=small|pipe|v5 pins one (testing; v5 only where it applies).
 bool use_pipe(int64_t M, int64_t N) {
   if (const char* f = getenv("NVFP4_GEMM_KERNEL")) {
-    if (!strcmp(f, "pipe")) return true;
+    if (!strcmp(f, "pipe") || !strcmp(f, "v5")) return true;
     if (!strcmp(f, "small")) return false;
   }
   return M * N > (int64_t)256 * 256 * 128;
+}
+
+// v5 needs K % 128 == 0, 16-byte aligned code rows, 4-byte aligned scale
+// rows and code bytes below 4 GiB per operand (32-bit source offsets).
+bool v5_applies(int64_t M, int64_t N, int64_t K, uintptr_t code_bits, uintptr_t scale_bits) {
+  if (const char* f = getenv("NVFP4_GEMM_KERNEL"))
+    if (!strcmp(f, "pipe") || !strcmp(f, "small")) return false;
+  const int64_t limit = (int64_t)1 << 32;
+  return K % kVBK == 0 && (code_bits & 15) == 0 && (scale_bits & 3) == 0 && M * (K / 2) < limit &&
+         N * (K / 2) < limit;
 }
 
 struct SplitPlan {
@@ -855,6 +1388,55 @@ hipError_t launch_pipe(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   return hipGetLastError();
 }
 
+// Tail split for v5: as plan_split, with stages of 128 K, at least 3 and at
+// most 8 ways (each way adds a slice of partial sums to write and read back;
+// the DiT up projection's 96 tail tiles would split only 2 ways, which
+// measured slower than computing them whole).
+SplitPlan plan_split_v5(int64_t M, int64_t N, int64_t K) {
+  SplitPlan p;
+  p.tiles = p.main_tiles = ((M + kVBM - 1) / kVBM) * ((N + kVBN - 1) / kVBN);
+  if (p.tiles == 0 || K % kVBK != 0) return p;
+  const int cus = compute_units();
+  const int64_t nk = K / kVBK;
+  const int64_t tail = p.tiles % cus;
+  if (tail == 0) return p;
+  int64_t ways = std::min<int64_t>(std::min<int64_t>(cus / tail, nk / 4), 8);
+  if (ways < 3) ways = 1;
+  if (const char* f = getenv("NVFP4_GEMM_SPLIT")) ways = std::min<int64_t>(atoi(f), nk);
+  if (ways < 2) return p;
+  p.tail = tail;
+  p.main_tiles = p.tiles - tail;
+  p.ways = (int)ways;
+  p.bytes = (size_t)tail * ways * kVBM * kVBN * sizeof(float);
+  return p;
+}
+
+hipError_t launch_v5(const uint8_t* a_codes, const uint8_t* a_scales, const float* sa,
+                     const uint8_t* w_codes, const uint8_t* w_scales, const float* sw,
+                     const void* bias, int64_t M, int64_t N, int64_t K, int epi, const Out& out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const SplitPlan plan = plan_split_v5(M, N, K);
+  const bool split = plan.ways > 1 && workspace && workspace_bytes >= plan.bytes;
+  const SplitK sk = split ? SplitK{static_cast<float*>(workspace), plan.main_tiles, plan.ways}
+                          : SplitK{nullptr, plan.tiles, 1};
+  const int64_t grid = split ? plan.main_tiles + plan.tail * plan.ways : plan.tiles;
+  const uint16_t* b16 = reinterpret_cast<const uint16_t*>(bias);
+  if (out.codes) {   // NVFP4 output: whole tiles
+    const SplitK whole{nullptr, plan.tiles, 1};
+    hipLaunchKernelGGL(gemm_nvfp4_v5_kernel<true>, dim3((unsigned)plan.tiles), dim3(kVNT), 0, stream,
+                       a_codes, a_scales, sa, w_codes, w_scales, sw, b16, M, N, K, epi, out, whole);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(gemm_nvfp4_v5_kernel<false>, dim3((unsigned)grid), dim3(kVNT), 0, stream, a_codes,
+                     a_scales, sa, w_codes, w_scales, sw, b16, M, N, K, epi, out, sk);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  hipLaunchKernelGGL(v5_split_reduce_kernel, dim3((unsigned)(plan.tail * kV5ReduceWgs)), dim3(256), 0,
+                     stream, static_cast<const float*>(workspace), plan.main_tiles, plan.ways, sa, sw,
+                     b16, M, N, epi, out.y, out.y_amax);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int compute_units() {
@@ -867,7 +1449,8 @@ int compute_units() {
 
 size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || !use_pipe(M, N)) return 0;
-  return plan_split(M, N, K).bytes;
+  // the plan of the kernel that runs with aligned operands
+  return v5_applies(M, N, K, 0, 0) ? plan_split_v5(M, N, K).bytes : plan_split(M, N, K).bytes;
 }
 
 namespace {
@@ -883,6 +1466,11 @@ hipError_t launch_any(const uint8_t* a_codes, const uint8_t* a_scales, const flo
     if (e != hipSuccess) return e;
   }
   if (M == 0 || N == 0) return hipSuccess;
+  const uintptr_t code_bits = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(w_codes);
+  const uintptr_t scale_bits = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(w_scales);
+  if (use_pipe(M, N) && v5_applies(M, N, K, code_bits, scale_bits))
+    return launch_v5(a_codes, a_scales, sa, w_codes, w_scales, sw, bias, M, N, K, epilogue, out,
+                     workspace, workspace_bytes, stream);
   if (use_pipe(M, N))
     return launch_pipe(a_codes, a_scales, sa, w_codes, w_scales, sw, bias, M, N, K, epilogue, out,
                        workspace, workspace_bytes, stream);

@@ -351,6 +351,44 @@ def test_gemm_kernels_and_k_split(monkeypatch, M, N, K, kernel, split):
     assert_gemm_close(y, ref, f"{kernel}/{split} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 520, 1152), (257, 300, 1024), (64, 33, 3072),
+                                   (513, 256, 128), (256, 256, 256), (600, 700, 384)])
+@pytest.mark.parametrize("split", [None, "3", "7"])
+def test_gemm_v5_and_k_split(monkeypatch, M, N, K, split):
+    # the direct-to-LDS kernel (K % 128 == 0) on ragged tiles, 1 to 9 stages,
+    # whole and with the tail tiles' K range split over 3 or 7 workgroups
+    monkeypatch.setenv("NVFP4_GEMM_KERNEL", "v5")
+    if split:
+        if int(split) > K // 128:
+            pytest.skip("fewer stages than ways")
+        monkeypatch.setenv("NVFP4_GEMM_SPLIT", split)
+        assert nv.gemm_workspace(M, N, K) is not None
+    for epi, bias in (("none", False), ("gelu", True)):
+        y, ref = _gemm_case(M, N, K, seed=M + 5 * N + K, bias=bias, epilogue=epi)
+        assert_gemm_close(y, ref, f"v5/{split} {M}x{N}x{K} {epi}")
+
+
+def test_gemm_v5_amax_and_determinism(monkeypatch):
+    import torch
+    monkeypatch.setenv("NVFP4_GEMM_KERNEL", "v5")
+    M, N, K = 700, 600, 1280
+    a_bits = W.random_matrix(91, (M, K), "t3")
+    w_bits = W.random_matrix(92, (N, K), "normal", 0.02)
+    qa, ra = check_quantize(a_bits)
+    qw, rw = check_quantize(w_bits)
+    for split in (None, "4"):
+        if split:
+            monkeypatch.setenv("NVFP4_GEMM_SPLIT", split)
+        ws = nv.gemm_workspace(M, N, K)
+        amax = torch.full((1,), 1e30, dtype=torch.float32, device="cuda")
+        y1 = bits_of(nv.gemm(qa, qw, epilogue="gelu", y_amax=amax, workspace=ws))
+        assert np.float32(amax.item()) == np.abs(bf16_bits_to_f32(y1)).max()
+        y2 = bits_of(nv.gemm(qa, qw, epilogue="gelu", workspace=ws))
+        assert np.array_equal(y1, y2)
+        ref, _ = gemm_fp64(ra, rw, K, gelu=True)
+        assert_gemm_close(y1, ref, f"v5 split {split}")
+
+
 def test_gemm_k_split_deterministic_with_amax(monkeypatch):
     import torch
     monkeypatch.setenv("NVFP4_GEMM_KERNEL", "pipe")
@@ -390,8 +428,9 @@ def _gemm_quantized_case(M, N, K, seed, amax_factor, epilogue="none", bias=False
     return y, static, fused, two_step
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 528, 1088), (257, 16, 64), (64, 1024, 2048)])
-@pytest.mark.parametrize("kernel", ["small", "pipe"])
+@pytest.mark.parametrize("M,N,K", [(300, 528, 1088), (257, 16, 64), (64, 1024, 2048),
+                                   (300, 528, 1152), (257, 16, 128)])
+@pytest.mark.parametrize("kernel", ["small", "pipe", "v5"])
 def test_gemm_quantized_equals_gemm_then_quantize(monkeypatch, M, N, K, kernel):
     monkeypatch.setenv("NVFP4_GEMM_KERNEL", kernel)
     for factor, epi, bias in ((1.0, "gelu", True), (0.25, "none", False), (8.0, "none", True)):
@@ -411,9 +450,12 @@ def torch_equal(u, v):
     return bool(torch.equal(u, v))
 
 
-def test_gemm_quantized_mlp_up_full_size():
+@pytest.mark.parametrize("kernel", ["default", "pipe"])
+def test_gemm_quantized_mlp_up_full_size(monkeypatch, kernel):
     # H of the MLP at 2048^2 written straight in NVFP4 under a static amax
     import torch
+    if kernel != "default":
+        monkeypatch.setenv("NVFP4_GEMM_KERNEL", kernel)
     x_bits = _mlp()["x"]
     wu_bits, _ = _oracle_weight("w_up")
     qx, qwu = gpu_quantize(x_bits), gpu_quantize(wu_bits)
