@@ -409,6 +409,39 @@ __device__ __forceinline__ void dma_stage(const uint8_t* __restrict__ a, const u
   }
 }
 
+// 32 rows x 128 columns of a wave's tile, staged in LDS by the epilogue of
+// gemm_fp8_dma_kernel, to bf16: lane takes 4 consecutive columns of a row per
+// step (32 lanes cover the row segment, so the 8-byte stores complete whole
+// lines).
+template <int EPI>
+__device__ __forceinline__ void fp8_slice_out(const float* st, const float* rs, f32x4 cs, f32x4 bv,
+                                              int64_t row0, int64_t col, int64_t M, int64_t N,
+                                              bool vec, uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63, c = lane & 31;
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int rr = it * 2 + (lane >> 5);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(st + rr * 128 + ((c ^ rr) << 2));
+    const float rsc = rs[rr];
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v[t] = __builtin_fmaf(a[t], rsc * cs[t], bv[t]);
+      if (EPI == 1) v[t] = gelu_erf(v[t]);
+    }
+    const u32x2 pk = {bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+    const int64_t row = row0 + rr;
+    if (vec) {
+      *reinterpret_cast<u32x2*>(y + row * N + col) = pk;
+    } else if (row < M) {
+      const uint16_t hv[4] = {(uint16_t)pk.x, (uint16_t)(pk.x >> 16), (uint16_t)pk.y, (uint16_t)(pk.y >> 16)};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (col + t < N) y[row * N + col + t] = hv[t];
+    }
+  }
+}
+
 __global__ __launch_bounds__(kDNT, 1) void gemm_fp8_dma_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ da, const uint8_t* __restrict__ w,
     const float* __restrict__ dw, const uint16_t* __restrict__ bias, int64_t M, int64_t N,
@@ -484,40 +517,38 @@ __global__ __launch_bounds__(kDNT, 1) void gemm_fp8_dma_kernel(
     return;
   }
 
-  // epilogue: (acc * (dA[m] * dW[n]) + bias) -> GELU -> bf16 (the operations
-  // of gemm_fp8_kernel's epilogue, in the same order)
+  // epilogue: (acc * (dA[m] * dW[n]) + bias) -> GELU -> bf16, the operations
+  // of gemm_fp8_kernel's epilogue in the same order.  Fully unrolled over 256
+  // accumulators per lane this would be more code than the instruction cache
+  // holds, so each wave moves 32 rows of its accumulators at a time into its
+  // own 16 KB of LDS (fp32, 16-byte chunks of a 512-byte row permuted by XOR
+  // with the row) and a short loop takes them back 4 columns per lane.
+  __syncthreads();   // every wave is done with the stage buffers
+  float* st = reinterpret_cast<float*>(lds0 + wave * 16384);
   const bool vec = m0 + kDBM <= M && n0 + kDBN <= N && N % 4 == 0 &&
                    (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+  const int cq = wn * kDWN + (lane & 31) * 4;             // this lane's 4 columns on read-back
+  const f32x4 cs = *reinterpret_cast<const f32x4*>(col_scale + cq);
+  const f32x4 bv = *reinterpret_cast<const f32x4*>(col_bias + cq);
 #pragma unroll
   for (int i = 0; i < kDTM; ++i) {
-    const int rl = wm * kDWM + i * 32 + r;
-    const int64_t row = m0 + rl;
-    const float rs = row_scale[rl];
-    uint16_t* __restrict__ yrow = y + row * N + n0;
 #pragma unroll
     for (int j = 0; j < kDTN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int cl = wn * kDWN + j * 32 + g * 8 + h * 4;
-        const f32x4 cs = *reinterpret_cast<const f32x4*>(col_scale + cl);
-        const f32x4 bv = *reinterpret_cast<const f32x4*>(col_bias + cl);
-        float v[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          v[t] = __builtin_fmaf(acc[i][j][4 * g + t], rs * cs[t], bv[t]);
-          if (epi == 1) v[t] = gelu_erf(v[t]);
-        }
-        const u32x2 pk = {bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
-        if (vec) {
-          *reinterpret_cast<u32x2*>(yrow + cl) = pk;
-        } else if (row < M) {
-          const uint16_t hv[4] = {(uint16_t)pk.x, (uint16_t)(pk.x >> 16), (uint16_t)pk.y,
-                                  (uint16_t)(pk.y >> 16)};
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            if (n0 + cl + t < N) yrow[cl + t] = hv[t];
-        }
+        const int c = j * 8 + g * 2 + h;
+        *reinterpret_cast<f32x4*>(st + r * 128 + ((c ^ r) << 2)) =
+            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
       }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    const int rl0 = wm * kDWM + i * 32;
+    if (epi == 1)
+      fp8_slice_out<1>(st, row_scale + rl0, cs, bv, m0 + rl0, n0 + cq, M, N, vec, y);
+    else
+      fp8_slice_out<0>(st, row_scale + rl0, cs, bv, m0 + rl0, n0 + cq, M, N, vec, y);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
