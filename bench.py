@@ -180,12 +180,13 @@ def main():
                              steps=args.steps, warmup=args.warmup)
     static = None if args.no_extras else static_section(extras)
     fp8 = None if args.no_extras else fp8_section(extras)
+    yardstick = None if args.no_extras else yardstick_section(extras)
 
     # roofline of the dominant kernel: the up GEMM
     up_us = stage_us["gemm_up_gelu_amax"]
     achieved = GEMM_FLOP / (up_us * 1e-6) / 1e12
-    traffic = measured_traffic("gemm_nvfp4_pipe_kernel", 2)
-    roofline = {"kernel": "gemm_nvfp4_pipe_kernel 256x256 (up projection, GELU + amax epilogue)",
+    traffic = measured_traffic("gemm_nvfp4_v5_kernel", 2)
+    roofline = {"kernel": "gemm_nvfp4_v5_kernel 256x256, 4 waves (up projection, GELU + amax epilogue)",
                 "bound": "mfma",
                 "achieved": round(achieved, 1), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_MFMA_F16, 4), "traffic": traffic,
@@ -269,6 +270,7 @@ def main():
         "roofline": roofline,
         "quantize": quant,
         "bf16_passthrough": bf16_pass,
+        "mfma_yardstick": yardstick,
         "static_scale": static,
         "fp8_rowwise": fp8,
         "graphs": graphs,
@@ -354,6 +356,29 @@ def fp8_section(c):
                                  "achieved": round(up, 1), "frac": round(up / PEAK_MFMA_FP8, 4)},
             "quantize_x_GBps": round(TOKENS * HIDDEN * 3 / st["quantize_x"] / 1e3, 1),
             "quantize_h_GBps": round(TOKENS * MLP * 3 / st["quantize_h"] / 1e3, 1)}
+
+
+def yardstick_section(c):
+    """What the vendor library reaches on the same GEMM shapes in plain fp16
+    (hipBLASLt through torch.matmul, no decode, no epilogue): the practical
+    matrix-core ceiling of this power-limited part, next to the 2.5 PF spec."""
+    import torch
+    out = {}
+    for name, (m, n, k) in (("gemm_up", (TOKENS, MLP, HIDDEN)), ("gemm_down", (TOKENS, HIDDEN, MLP))):
+        a = torch.randn(m, k, device=c.x.device).to(torch.float16)
+        w = torch.randn(n, k, device=c.x.device).to(torch.float16)
+        y = torch.empty(m, n, device=c.x.device, dtype=torch.float16)
+
+        def run(events, a=a, w=w, y=y):
+            mark = (lambda q: events[q].record(c.stream)) if events else (lambda q: None)
+            mark(0)
+            torch.matmul(a, w.t(), out=y)
+            mark(1)
+        _, st = timed_sequence(c, run, ["mm"])
+        flop = 2 * m * n * k
+        out[name] = {"shape": [m, n, k], "us": st["mm"], "TFLOPs": round(flop / (st["mm"] * 1e-6) / 1e12, 1)}
+        del a, w, y
+    return {"what": "hipBLASLt fp16 GEMM (torch.matmul), same shapes, no decode or epilogue", **out}
 
 
 def graph_section(to_dev, ev, stream):
