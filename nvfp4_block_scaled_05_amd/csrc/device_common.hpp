@@ -73,26 +73,28 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-// erf-form GELU, z * Phi(z) with Phi(z) = erfc(-z / sqrt 2) / 2.  erfc is the
-// Chebyshev fit "erfcc" of Numerical Recipes (section 6.2, fractional error
-// below 1.2e-7 for every argument), so the result is accurate relative to
-// |GELU(z)| in both tails; the remaining error is a few binary32 ulps from
-// the approximate reciprocal and exponential.
+// erf-form GELU, z * Phi(z) with Phi(z) = erfc(-z / sqrt 2) / 2.  With
+// x = |z| / sqrt 2 and t = 1 / (1 + |z| / (2 sqrt 2)), erfc(x) / 2 is
+// t * 2^(Q(t) - 1 - z^2 log2(e) / 2), Q a degree-7 polynomial fitted to
+// log2(erfcx(x) / t) on |z| <= 14 (fractional error of erfc below 7e-7;
+// gelu_fit.py beside this file derives the coefficients; the constant term
+// below includes the -1).  The result is accurate relative to |GELU(z)| in
+// both tails; what remains is a few binary32 ulps from the approximate
+// reciprocal and exponential and, far in the negative tail, the rounding of
+// the exponent's argument.
 __device__ __forceinline__ float gelu_erf(float z) {
-  const float x = __builtin_fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, x, 1.0f));
-  float q = 0.17087277f;
-  q = __builtin_fmaf(q, t, -0.82215223f);
-  q = __builtin_fmaf(q, t, 1.48851587f);
-  q = __builtin_fmaf(q, t, -1.13520398f);
-  q = __builtin_fmaf(q, t, 0.27886807f);
-  q = __builtin_fmaf(q, t, -0.18628806f);
-  q = __builtin_fmaf(q, t, 0.09678418f);
-  q = __builtin_fmaf(q, t, 0.37409196f);
-  q = __builtin_fmaf(q, t, 1.00002368f);
-  const float arg = __builtin_fmaf(t, q, __builtin_fmaf(-x, x, -1.26551223f));
-  const float y = t * __builtin_amdgcn_exp2f(arg * 1.44269504088896341f);   // erfc(x)
-  return z * (z >= 0.0f ? __builtin_fmaf(-0.5f, y, 1.0f) : 0.5f * y);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_fabsf(z), 0.353553391f, 1.0f));
+  float q = -0.26468796f;
+  q = __builtin_fmaf(q, t, 1.0576829f);
+  q = __builtin_fmaf(q, t, -1.397297f);
+  q = __builtin_fmaf(q, t, 0.46071547f);
+  q = __builtin_fmaf(q, t, -0.03360385f);
+  q = __builtin_fmaf(q, t, 0.5611624f);
+  q = __builtin_fmaf(q, t, 1.4417965f);
+  q = __builtin_fmaf(q, t, -2.8257694f);
+  const float arg = __builtin_fmaf(z * -0.72134752f, z, q);
+  const float h = t * __builtin_amdgcn_exp2f(arg);           // erfc(x) / 2 = Phi(-|z|)
+  return z * (z < 0.0f ? h : 1.0f - h);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
