@@ -781,8 +781,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_pipe_kernel(
 //     during stage t, after its packed operands have all been read into
 //     registers, so no LDS read waits on a load in flight.
 //   * The decode of step s+1 is interleaved with the MFMAs of step s; the
-//     MFMAs of a stage's last step run after the next barrier, while the next
-//     stage's LDS reads are in flight.
+//     MFMAs of a stage's last two steps run after the next barrier, while the
+//     next stage's LDS reads, scale conversion and first decode are done.
 //   * The weight fragment is the MFMA's first operand, so acc[i][j] holds the
 //     transposed tile: lane (r, h) has row m = i*32 + r and the four
 //     consecutive columns n = j*32 + 8g + 4h + t at elements 4g + t.
@@ -914,16 +914,24 @@ __device__ __forceinline__ void v5_step(const V5Packed& p, const V5Ops& cur, V5O
   }
 }
 
-// Steps 1-7 of a stage whose step-0 operands are in `o0`; leaves step 7's in `o1`.
-__device__ __forceinline__ void v5_steps(const V5Packed& p, V5Ops& o0, V5Ops& o1,
-                                         f32x16 (&acc)[kVTM][kVTN]) {
-  v5_step<1>(p, o0, o1, acc);
-  v5_step<2>(p, o1, o0, acc);
-  v5_step<3>(p, o0, o1, acc);
-  v5_step<4>(p, o1, o0, acc);
-  v5_step<5>(p, o0, o1, acc);
-  v5_step<6>(p, o1, o0, acc);
-  v5_step<7>(p, o0, o1, acc);
+// Steps of a stage whose step-0 operands are in `y` (`x` free): the MFMAs of
+// steps 0-5 and the decode of steps 1-7.  Leaves step 6's operands in `y`,
+// step 7's in `c`, and `x` free: those two steps run after the next barrier.
+__device__ __forceinline__ void v5_body(const V5Packed& p, V5Ops& x, V5Ops& y, V5Ops& c,
+                                        f32x16 (&acc)[kVTM][kVTN]) {
+  v5_step<1>(p, y, x, acc);
+  v5_step<2>(p, x, y, acc);
+  v5_step<3>(p, y, x, acc);
+  v5_step<4>(p, x, y, acc);
+  v5_step<5>(p, y, x, acc);
+  v5_decode<6>(p, y);                      // MFMAs of step 5 with two decodes
+  v5_decode<7>(p, c);
+  v5_mfma(x, acc);
+#pragma unroll
+  for (int m = 0; m < kVTM * kVTN; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU (decode)
+  }
 }
 
 // Stage data in LDS: this wave's loads for it have landed (vmcnt; with
@@ -942,29 +950,42 @@ __device__ __forceinline__ void v5_barrier(bool next_in_flight) {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// One stage after the first, from slot `cur`: read all of its packed operands
-// (so no LDS read follows the loads issued below), run the previous stage's
-// last MFMAs while the reads are in flight, issue the loads of the stage two
-// ahead into `refill`, then this stage's steps.
+// One stage after the first, from slot `cur`.  The previous stage left the
+// operands of its steps 6 and 7 in `s6` and `c`; their 32 MFMAs run here,
+// first while this stage's packed operands are read (all of them, so no LDS
+// read follows the loads issued below), then while its scales are converted
+// and step 0 decoded into `x`, so the matrix pipe stays busy across the
+// barrier.  The loads of the stage two ahead go into `refill`.  Leaves this
+// stage's step 6 in `x`, step 7 in `c`; `s6` is free (roles swap each stage).
 __device__ __forceinline__ void v5_stage(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
                                          const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
                                          const V5Src& src, const uint8_t* cur, uint8_t* refill,
                                          bool next_in_flight, bool do_refill, int k_refill, int a_row,
-                                         int w_row, int h, int x, V5Packed& p, V5Ops& o0, V5Ops& o1,
-                                         f32x16 (&acc)[kVTM][kVTN]) {
+                                         int w_row, int h, int x_sw, V5Packed& p, V5Ops& x, V5Ops& s6,
+                                         V5Ops& c, f32x16 (&acc)[kVTM][kVTN]) {
   v5_barrier(next_in_flight);
   uint32_t sc[8];
-  v5_read(cur, a_row, w_row, h, x, p, sc);
-  v5_mfma(o1, acc);                        // previous stage, step 7
+  v5_read(cur, a_row, w_row, h, x_sw, p, sc);
+  v5_mfma(s6, acc);                        // previous stage, step 6
+#pragma unroll
+  for (int m = 0; m < 12; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (do_refill) v5_issue(ac, as, wc, ws, src, k_refill, refill);
+  v5_scales(sc, p);
+  v5_decode<0>(p, x);
+  v5_mfma(c, acc);                         // previous stage, step 7
 #pragma unroll
   for (int m = 0; m < kVTM * kVTN; ++m) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU (scales, decode, addresses)
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (loads)
   }
-  if (do_refill) v5_issue(ac, as, wc, ws, src, k_refill, refill);
-  v5_scales(sc, p);
-  v5_decode<0>(p, o0);
-  v5_steps(p, o0, o1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  v5_body(p, s6, x, c, acc);
 }
 
 // Epilogue of v5: acc * sA*sW + bias (one fused multiply-add), optional GELU,
@@ -1178,7 +1199,7 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
   const int ke = split < 0 ? nk : (int)((int64_t)(split + 1) * nk / sk.ways);
   const int ns = ke - kb;
   V5Packed p;
-  V5Ops o0, o1;
+  V5Ops oa, ob, oc;
   // stage kb + t lives in slot t % 3
   v5_issue(a_codes, a_scales, w_codes, w_scales, src, kb, lds);
   if (ns > 1) v5_issue(a_codes, a_scales, w_codes, w_scales, src, kb + 1, lds + kVStage);
@@ -1189,14 +1210,18 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
     if (ns > 2) v5_issue(a_codes, a_scales, w_codes, w_scales, src, kb + 2, lds + 2 * kVStage);
     v5_scales(sc, p);
   }
-  v5_decode<0>(p, o0);
-  v5_steps(p, o0, o1, acc);
+  v5_decode<0>(p, oa);
+  v5_body(p, ob, oa, oc, acc);             // steps 6, 7 pending in oa, oc
+  // each stage leaves its step 6 in the set it decoded step 0 into; one copy
+  // per stage puts it back where the next stage expects it
   for (int t = 1; t < ns; ++t) {
-    const int slot = t % 3, rslot = (t + 2) % 3;
-    v5_stage(a_codes, a_scales, w_codes, w_scales, src, lds + slot * kVStage, lds + rslot * kVStage,
-             t + 1 < ns, t + 2 < ns, kb + t + 2, a_row, w_row, h, x, p, o0, o1, acc);
+    v5_stage(a_codes, a_scales, w_codes, w_scales, src, lds + (t % 3) * kVStage,
+             lds + ((t + 2) % 3) * kVStage, t + 1 < ns, t + 2 < ns, kb + t + 2, a_row, w_row, h, x,
+             p, ob, oa, oc, acc);
+    oa = ob;
   }
-  v5_mfma(o1, acc);
+  v5_mfma(oa, acc);
+  v5_mfma(oc, acc);
 
   if (!kQuant && split >= 0) {
     // a tail split: fp32 partial sums into its slice in accumulator order --
