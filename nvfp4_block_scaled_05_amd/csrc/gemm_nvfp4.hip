@@ -799,6 +799,14 @@ constexpr int kVSA = kVW + kVBN * kVCodeRow;        // A scales
 constexpr int kVSW = kVSA + kVBM * kVScaleRow;      // W scales
 constexpr int kVStage = kVSW + kVBN * kVScaleRow;   // 36 KB
 
+// Index of this wave in the workgroup as a scalar (the compiler cannot see
+// that threadIdx.x >> 6 is uniform across a wave): LDS destinations of the
+// global->LDS loads, which go through M0, are then computed in scalar
+// registers instead of one v_readfirstlane per load.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // This lane's source offsets (bytes from the start of the operand's codes /
 // scales; rows * K / 2 < 2^32 is checked on the host).
 struct V5Src {
@@ -832,7 +840,7 @@ __device__ __forceinline__ void v5_setup(int64_t M, int64_t N, int64_t K, int64_
 __device__ __forceinline__ void v5_issue(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
                                          const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
                                          const V5Src& d, int kt, uint8_t* stage) {
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const uint8_t* ack = ac + (int64_t)kt * kVCodeRow;
   const uint8_t* wck = wc + (int64_t)kt * kVCodeRow;
   const uint8_t* ask = as + (int64_t)kt * kVScaleRow;
