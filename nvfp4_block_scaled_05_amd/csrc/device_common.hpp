@@ -145,6 +145,14 @@ __device__ __forceinline__ f16x8 decode8(uint32_t w, _Float16 s) {
                                          __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
 }
 
+// Index of this wave in the workgroup as a scalar (the compiler cannot see
+// that threadIdx.x >> 6 is uniform across a wave): LDS destinations of the
+// global->LDS loads, which go through M0, are then computed in scalar
+// registers instead of one v_readfirstlane per load.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {

@@ -323,7 +323,7 @@ __device__ __forceinline__ void dma_setup(int64_t M, int64_t N, int64_t K, int64
 
 __device__ __forceinline__ void dma_issue(const uint8_t* __restrict__ a, const uint8_t* __restrict__ w,
                                           const DmaPtrs& d, int64_t k0, uint8_t* stage) {
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const uint8_t* ak = a + k0;
   const uint8_t* wk = w + k0;
 #pragma unroll

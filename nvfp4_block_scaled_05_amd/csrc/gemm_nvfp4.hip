@@ -799,14 +799,6 @@ constexpr int kVSA = kVW + kVBN * kVCodeRow;        // A scales
 constexpr int kVSW = kVSA + kVBM * kVScaleRow;      // W scales
 constexpr int kVStage = kVSW + kVBN * kVScaleRow;   // 36 KB
 
-// Index of this wave in the workgroup as a scalar (the compiler cannot see
-// that threadIdx.x >> 6 is uniform across a wave): LDS destinations of the
-// global->LDS loads, which go through M0, are then computed in scalar
-// registers instead of one v_readfirstlane per load.
-__device__ __forceinline__ int wave_id() {
-  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-}
-
 // This lane's source offsets (bytes from the start of the operand's codes /
 // scales; rows * K / 2 < 2^32 is checked on the host).
 struct V5Src {
