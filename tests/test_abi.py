@@ -104,8 +104,12 @@ def test_gemm_workspace_bytes(lib):
     assert wb(128, 1024, 1024) == 0
     # DiT MLP projections at 2048^2 with a CFG pair: the tiles past the last
     # whole round over the compute units are split over K
-    down = wb(16896, 3072, 12288)       # 792 tiles: 24 past 3 rounds, split 10 ways
-    assert 0 < down <= 64 << 20 and down % (256 * 1024) == 0
+    # 792 tiles: 24 past 3 rounds over 256 compute units, split 8 ways (the
+    # direct-to-LDS kernel's cap; 96 stages of 128 would allow more)
+    assert wb(16896, 3072, 12288) == 24 * 8 * 256 * 256 * 4
+    # K % 128 != 0 runs the register-staged kernel, whose stages are 64 wide:
+    # 24 tail tiles, 10 ways
+    assert wb(16896, 3072, 12288 + 64) == 24 * 10 * 256 * 256 * 4
     # 3168 tiles: 96 past 12 rounds would split only 2 ways, not worth it
     assert wb(16896, 12288, 3072) == 0
     # a whole number of rounds: nothing to split
