@@ -80,8 +80,9 @@ int nvfp4_abi_version(void);
 const char* nvfp4_status_string(int status);
 
 /* Bytes of device workspace nvfp4_quantize needs for a [rows, cols] input when
- * it computes the tensor amax itself (amax_in == NULL): 4 bytes per partial
- * maximum, at most 4096 bytes.  0 when rows or cols is not positive. */
+ * it computes the tensor amax itself (amax_in == NULL): 4096 (partial maxima
+ * and, for the single-pass kernel, its arrival counters and flags).  0 when
+ * rows or cols is not positive. */
 size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
@@ -116,6 +117,15 @@ size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
  *   else e_b = 1 / (S_b * s_dec), code = sign | E2M1(|x| * e_b), nearest-even,
  *     saturating at 6.
  * Deterministic: the same input gives the same bytes on every call.
+ * When the amax is computed here and the tensor has at least 25.2 M
+ * elements and fits on chip (at most 212,992 elements per compute unit: 54.5 M
+ * elements, 109 MB of bf16, on 256 units), it is read from HBM once: one
+ * workgroup per compute unit holds its share on chip while the amax is
+ * agreed, then encodes it.  The workgroups of that kernel wait for each other; if another
+ * stream's work keeps some of them from starting, the waiting ones time out
+ * after 200 us and compute the amax themselves, so the call still completes
+ * with the same bytes, only slower.  Other sizes take two passes over the
+ * input.  NVFP4_QUANT_KERNEL=twopass (environment) forces the two passes.
  */
 int nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols,
                    uint8_t* codes, uint8_t* scales, float* tensor_scale,

@@ -51,6 +51,16 @@ int nvfp4_probe_decode(const uint32_t* words, const uint32_t* sbytes, int n, uin
  * epilogue's erf-form GELU. */
 int nvfp4_probe_bf16_gelu(const float* in, int n, uint16_t* bf16, float* gelu, void* stream);
 
+/* For n bf16 patterns h = bits[i] & 0xFFFF (4-byte aligned outputs):
+ *   quot[i]       = the quantizer's a / 6 of a = |h| (one multiply, two FMA
+ *                   corrections);
+ *   scale[i]      = its block scale byte E4M3((a / 6) * s_enc) through the
+ *                   clamp and the hardware conversion;
+ *   zero_codes[i] = the packed E2M1 codes of eight copies of h encoded with
+ *                   factor 0 (a block whose scale byte is 0). */
+int nvfp4_probe_block_scale(const uint32_t* bits, int n, float s_enc, float* quot,
+                            uint32_t* scale, uint32_t* zero_codes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

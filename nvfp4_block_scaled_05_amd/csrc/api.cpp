@@ -68,7 +68,9 @@ const char* nvfp4_status_string(int status) {
 
 size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || bad_dim(rows) || bad_dim(cols)) return 0;
-  return 4u * (size_t)nvfp4::amax_partial_count(rows * cols);
+  // the two-pass kernels use one word per partial maximum, the single-pass
+  // kernel three counter words and one partial per compute unit
+  return 4u * (size_t)nvfp4::kMaxAmaxPartials;
 }
 
 int nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes,
@@ -89,7 +91,8 @@ int nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* code
   if (st != NVFP4_OK) return st;
   if (empty) return NVFP4_OK;
   return hip_status(nvfp4::launch_quantize(x_bf16, rows, cols, codes, scales, tensor_scale,
-                                           amax_in, static_cast<uint32_t*>(workspace), dev_status,
+                                           amax_in, static_cast<uint32_t*>(workspace),
+                                           workspace_bytes, dev_status,
                                            static_cast<hipStream_t>(stream)));
 }
 

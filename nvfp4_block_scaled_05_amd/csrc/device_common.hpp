@@ -173,6 +173,12 @@ __device__ __forceinline__ u16x2 max8(u32x4 a) {
                    max_u16x2(abs_halves(a.z), abs_halves(a.w)));
 }
 
+// Max |x| of a 16-element block (two 16-byte words) as a 16-bit bf16 magnitude.
+__device__ __forceinline__ uint32_t block_max_bits(u32x4 lo, u32x4 hi) {
+  const u16x2 m = max_u16x2(max8(lo), max8(hi));
+  return m.x > m.y ? m.x : m.y;
+}
+
 // Per-tensor scales from the tensor amax (a finite binary32): s_enc = 2688 /
 // amax and s_dec = 1 / s_enc, both correctly rounded; below 2^-96 the tensor
 // is degenerate (s_enc = s_dec = 1, every block scale 0).
@@ -203,6 +209,44 @@ __device__ __forceinline__ uint32_t signs8(u32x4 v) {
     c |= ((w[j] >> 31) & 1u) << (8 * j + 7);
   }
   return c;
+}
+
+// a / 6 in binary32, correctly rounded, for every bf16 value a >= 0: one
+// multiply by RN(1/6) and two FMA corrections.  (Not for every binary32: some
+// subnormal quotients differ; an exhaustive comparison over the bf16
+// magnitudes with the IEEE division finds no difference.)
+__device__ __forceinline__ float div6_bf16(float a) {
+  const float c = 0x1.555556p-3f;
+  const float q0 = a * c;
+  const float r = __builtin_fmaf(-q0, 6.0f, a);
+  return __builtin_fmaf(r, c, q0);
+}
+
+// Block scale byte E4M3_RNE_sat((a_b / 6) * s_enc) for a bf16 block max a_b:
+// the same byte as e4m3_from_f32_rne, through the clamp and the packed
+// hardware conversion.
+__device__ __forceinline__ uint32_t block_scale_e4m3(float a_b, float s_enc) {
+  const float t = div6_bf16(a_b) * s_enc;
+  return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(t, 448.0f), 0.0f, 0, false) & 0xFFu;
+}
+
+// Encode factor e_S = 1 / (S * s_dec) of scale byte S (1..126), correctly
+// rounded; 0 for S = 0, which makes encode8 give the sign-only codes (every
+// product is a signed zero, and the conversion keeps the sign of zero).
+// Kernels tabulate it once per tensor: 126 values replace a division per block.
+__device__ __forceinline__ float encode_factor(uint32_t S, float s_dec) {
+  return S == 0 || S > 0x7Eu ? 0.0f : 1.0f / (e4m3_to_f32(S) * s_dec);
+}
+
+// One 16-element block whose bf16 max |x| is a_b: scale byte S and 8 bytes of
+// codes, with e_of[] the encode factors of every scale byte.  The same bytes
+// as quantize_block.
+__device__ __forceinline__ void quantize_block_tab(u32x4 lo, u32x4 hi, float a_b, bool degenerate,
+                                                   float s_enc, const float* e_of, u32x2& c,
+                                                   uint32_t& S) {
+  S = degenerate ? 0u : block_scale_e4m3(a_b, s_enc);
+  const float e = e_of[S];
+  c = u32x2{encode8(lo, e), encode8(hi, e)};
 }
 
 // One 16-element block: scale byte and 8 bytes of codes.

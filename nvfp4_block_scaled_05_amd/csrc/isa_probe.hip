@@ -12,6 +12,9 @@
 //     conversion): the same scan, all four byte positions.
 //   * E2M1 decode to fp16 / fp32 and E4M3 decode to fp16 / fp32 (GEMM
 //     loader, dequantizer): every byte value in every byte position.
+//   * The block-scale path of the single-pass quantizer (a / 6 by FMA
+//     corrections, the hardware E4M3 conversion, encode factor 0 for scale
+//     byte 0): every bf16 pattern.
 #include "device_common.hpp"
 #include "nvfp4_isa_probe.h"
 
@@ -116,6 +119,23 @@ __global__ __launch_bounds__(256) void bf16_gelu_kernel(const float* in, int n, 
   if (i + (n + 1) / 2 < n) gelu[i + (n + 1) / 2] = gelu_erf(in[i + (n + 1) / 2]);
 }
 
+// For bf16 pattern h = bits[i] & 0xFFFF: quot[i] = div6_bf16(|h|) (the
+// quotient behind the block scale), scale[i] = block_scale_e4m3(|h|, s_enc),
+// zero_codes[i] = encode8 of eight copies of h with encode factor 0 (the
+// codes of a block whose scale byte is 0).
+__global__ __launch_bounds__(256) void block_scale_kernel(const uint32_t* bits, int n, float s_enc,
+                                                          float* quot, uint32_t* scale,
+                                                          uint32_t* zero_codes) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t h = bits[i] & 0xFFFFu;
+  const float a = bf16_bits_to_f32(h & 0x7FFFu);
+  quot[i] = div6_bf16(a);
+  scale[i] = block_scale_e4m3(a, s_enc);
+  const uint32_t w = h | (h << 16);
+  zero_codes[i] = encode8(u32x4{w, w, w, w}, 0.0f);
+}
+
 bool bad_ptr(const void* p) { return p == nullptr; }
 
 }  // namespace
@@ -171,6 +191,15 @@ int nvfp4_probe_bf16_gelu(const float* in, int n, uint16_t* bf16, float* gelu, v
   const int threads = (n + 1) / 2;
   hipLaunchKernelGGL(bf16_gelu_kernel, dim3((threads + 255) / 256), dim3(256), 0,
                      static_cast<hipStream_t>(stream), in, n, reinterpret_cast<uint32_t*>(bf16), gelu);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int nvfp4_probe_block_scale(const uint32_t* bits, int n, float s_enc, float* quot, uint32_t* scale,
+                            uint32_t* zero_codes, void* stream) {
+  if (bad_ptr(bits) || bad_ptr(quot) || bad_ptr(scale) || bad_ptr(zero_codes)) return -1;
+  if (n <= 0) return -2;
+  hipLaunchKernelGGL(block_scale_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), bits, n, s_enc, quot, scale, zero_codes);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

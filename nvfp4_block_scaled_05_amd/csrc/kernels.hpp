@@ -16,7 +16,8 @@ int amax_partial_count(int64_t numel);
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, float* tensor_scale, const float* amax_in,
-                           uint32_t* workspace, int32_t* dev_status, hipStream_t stream);
+                           uint32_t* workspace, size_t workspace_bytes, int32_t* dev_status,
+                           hipStream_t stream);
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales,
                              const float* tensor_scale, int64_t rows, int64_t cols, void* y,

@@ -5,7 +5,10 @@
 // from the tensor amax, and one scale per block of 16 elements computed in the
 // same pass that encodes the elements.
 //
-// Quantization is two launches, both HBM-bound:
+// With the amax computed here, a tensor that fits on chip (up to 109 MB of
+// bf16 on 256 compute units) takes the single-pass kernel further down, which
+// reads it from HBM once; otherwise quantization is two launches, both
+// HBM-bound:
 //   amax_partial_kernel  every workgroup reads a grid-strided slice with
 //                        128-bit loads (ordinary loads, so the tensor stays in
 //                        the last-level cache for the second pass) and writes one partial max|x| (as the
@@ -23,6 +26,7 @@
 // off, so every value equals the CPU oracle's bit for bit.
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -101,6 +105,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
     *tensor_scale = s_dec;
     if (dev_status) *dev_status = 0;
   }
+  __shared__ float e_of[128];                      // encode factor of every scale byte
+  if (threadIdx.x < 128) e_of[threadIdx.x] = encode_factor(threadIdx.x, s_dec);
+  __syncthreads();
   const int64_t stride = (int64_t)gridDim.x * kQuantThreads * U;
   int64_t b = (int64_t)blockIdx.x * kQuantThreads * U + threadIdx.x;
   for (; b + (U - 1) * kQuantThreads < nblocks; b += stride) {
@@ -114,15 +121,17 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
     for (int u = 0; u < U; ++u) {
       u32x2 c;
       uint32_t S;
-      quantize_block(lo[u], hi[u], degenerate, s_enc, s_dec, c, S);
+      quantize_block_tab(lo[u], hi[u], bf16_bits_to_f32(block_max_bits(lo[u], hi[u])), degenerate,
+                         s_enc, e_of, c, S);
       codes[b + u * kQuantThreads] = c;
       scales[b + u * kQuantThreads] = (uint8_t)S;
     }
   }
   for (; b < nblocks; b += kQuantThreads) {
+    const u32x4 lo = x[2 * b], hi = x[2 * b + 1];
     u32x2 c;
     uint32_t S;
-    quantize_block(x[2 * b], x[2 * b + 1], degenerate, s_enc, s_dec, c, S);
+    quantize_block_tab(lo, hi, bf16_bits_to_f32(block_max_bits(lo, hi)), degenerate, s_enc, e_of, c, S);
     codes[b] = c;
     scales[b] = (uint8_t)S;
   }
@@ -151,6 +160,221 @@ __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
     }
     __builtin_nontemporal_store(u32x4{out[0], out[1], out[2], out[3]}, y + 2 * b);
     __builtin_nontemporal_store(u32x4{out[4], out[5], out[6], out[7]}, y + 2 * b + 1);
+  }
+}
+
+// Single-pass quantizer for a tensor that fits on chip.  One workgroup per
+// compute unit (its LDS use admits no second one).  Workgroup g owns the
+// contiguous blocks [g*chunk, (g+1)*chunk):
+//   1. it reads them all at once, R blocks per thread into registers and L
+//      per thread straight into LDS (global->LDS loads into a wave-private
+//      region), keeps each block's max|x| and folds them into one partial;
+//   2. it publishes the partial, counts itself in, and waits until every
+//      workgroup has arrived;
+//   3. it folds the partials into the tensor amax, derives s_enc / s_dec,
+//      tabulates the encode factor of every scale byte, and encodes its
+//      blocks from registers and LDS, so X crosses HBM once.
+// The bytes are those of quantize_block (quantize_block_tab computes the same
+// function).  The loads are unconditional: indexes past the range are clamped
+// to its last block (for an empty range, the tensor's last block), which the
+// maxima already count, so the compiler can overlap the maxima with the data
+// still arriving.  Codes and scales are streamed out with nontemporal stores.
+// The arrival (below) uses only agent-coherent atomic words.  The grid is not
+// launched cooperatively (that launch path costs tens of microseconds), so
+// nothing guarantees that all workgroups are resident together: another
+// stream's kernels may hold compute units.  The wait is therefore bounded in
+// time: a workgroup that has not been released after kResWaitTicks reads the
+// whole tensor for its amax itself (slow, but the same value), so the kernel
+// always completes and always gives the same bytes.
+static constexpr int kResThreads = 1024;
+static constexpr int kResR = 9;   // 16-element blocks per thread held in registers
+static constexpr int kResL = 4;   // ... and in LDS (4 * 32 B * 1024 = 128 KB)
+static constexpr uint64_t kResWaitTicks = 20000;   // 200 us of the 100 MHz real-time counter
+
+// Workspace words of the arrival: workgroups are dealt to kXcds groups
+// (blockIdx % 8, which is also the XCD they run on); each group counts its
+// arrivals on its own 128-byte line, the last of a group counts the group in
+// on the top counter, and the last group raises every group's release flag,
+// which that group's workgroups poll.  No line sees more than 32 arrivals or
+// pollers.  The counters and flags are cleared by a one-workgroup kernel
+// just before; the partials follow them.
+static constexpr int kResLine = 32;                              // words per 128-byte line
+static constexpr int kResTop = 0;                                // top counter
+static constexpr int kResGroupCount = kResLine;                  // + 32 * g
+static constexpr int kResGroupFlag = kResLine * (1 + kXcds);     // + 32 * g
+static constexpr int kResPartials = kResLine * (1 + 2 * kXcds);  // + workgroup
+static constexpr int kResClearWords = kResPartials;
+
+__global__ __launch_bounds__(256) void clear_sync_kernel(uint32_t* p) {
+  for (int i = threadIdx.x; i < kResClearWords; i += 256) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(
+    const u32x4* __restrict__ x, uint32_t nblocks, uint32_t chunk, u32x2* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tensor_scale, int32_t* __restrict__ dev_status,
+    uint32_t* __restrict__ sync) {
+  constexpr int T = kResThreads, NW = T / 64, R = kResR, L = kResL;
+  __shared__ u32x4 stage[NW][L][128];   // wave w, slot s: 64 blocks = 128 words
+  __shared__ float e_of[128];           // encode factor of every scale byte
+  __shared__ uint32_t red[NW];
+  __shared__ uint32_t shared_amax, shared_ok;
+  const int wave = wave_id();
+  const int lane = threadIdx.x & 63;
+  const uint32_t lo = blockIdx.x * chunk;
+  const uint32_t end = lo + chunk < nblocks ? lo + chunk : nblocks;   // may be below lo: empty
+  const uint32_t last = end > lo ? end - 1 : nblocks - 1;
+
+  // 1. loads: the LDS part first (no registers held), then the register part
+#pragma unroll
+  for (int s = 0; s < L; ++s) {
+    const uint32_t blk0 = lo + (uint32_t)((R + s) * T + wave * 64);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t word = 2 * blk0 + (uint32_t)(64 * i + lane);
+      __builtin_amdgcn_global_load_lds(x + (word < 2 * last + 1 ? word : 2 * last + 1),
+                                       &stage[wave][s][64 * i], 16, 0, 0);
+    }
+  }
+  u32x4 a[R], b[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    uint32_t blk = lo + (uint32_t)(k * T) + threadIdx.x;
+    blk = blk < last ? blk : last;
+    a[k] = __builtin_nontemporal_load(x + 2 * blk);
+    b[k] = __builtin_nontemporal_load(x + 2 * blk + 1);
+  }
+  // block maxima, two 16-bit magnitudes per word
+  uint32_t bm[(R + L + 1) / 2];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const uint32_t v = block_max_bits(a[k], b[k]);
+    bm[k / 2] = k % 2 ? bm[k / 2] | (v << 16) : v;
+  }
+  __builtin_amdgcn_sched_barrier(0);    // the maxima above stay ahead of the wait below
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): the LDS part has landed
+#pragma unroll
+  for (int s = 0; s < L; ++s) {
+    const uint32_t v = block_max_bits(stage[wave][s][2 * lane], stage[wave][s][2 * lane + 1]);
+    const int k = R + s;
+    bm[k / 2] = k % 2 ? bm[k / 2] | (v << 16) : v;
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < (R + L + 1) / 2; ++k) {
+    const u16x2 p = __builtin_bit_cast(u16x2, bm[k]);
+    m = m > p.x ? m : p.x;
+    m = m > p.y ? m : p.y;
+  }
+
+  // 2. partial max of the workgroup, arrival, bounded wait
+  m = wave_max_u32(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) r = r > red[w] ? r : red[w];
+    // Only agent-coherent atomic words cross between workgroups (partials,
+    // counters, flags), so ordering needs no cache write-back: each store is
+    // complete (vmcnt) before the next word is touched, and the compiler may
+    // not swap them (signal fences).
+    __hip_atomic_store(sync + kResPartials + blockIdx.x, r << 16, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0070);             // vmcnt(0) lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const uint32_t grp = blockIdx.x % kXcds;
+    const uint32_t groups = gridDim.x < kXcds ? gridDim.x : kXcds;
+    const uint32_t in_group = (gridDim.x - grp + kXcds - 1) / kXcds;
+    if (__hip_atomic_fetch_add(sync + kResGroupCount + kResLine * grp, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) == in_group - 1 &&
+        __hip_atomic_fetch_add(sync + kResTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            groups - 1) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      for (uint32_t q = 0; q < groups; ++q)
+        __hip_atomic_store(sync + kResGroupFlag + kResLine * q, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool ok = true;
+    while (__hip_atomic_load(sync + kResGroupFlag + kResLine * grp, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kResWaitTicks) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    shared_ok = ok;
+  }
+  __syncthreads();
+  uint32_t r = 0;
+  if (shared_ok) {                                // the partials, one per thread
+    if (threadIdx.x < gridDim.x)
+      r = __hip_atomic_load(sync + kResPartials + threadIdx.x, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+    for (uint32_t i = threadIdx.x + T; i < gridDim.x; i += T) {
+      const uint32_t p = __hip_atomic_load(sync + kResPartials + i, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      r = r > p ? r : p;
+    }
+  } else {                                        // not all resident: read the whole tensor
+    u16x2 mm = {0, 0};
+    for (uint32_t w = threadIdx.x; w < 2 * nblocks; w += T) mm = max_u16x2(mm, max8(x[w]));
+    r = (uint32_t)(mm.x > mm.y ? mm.x : mm.y) << 16;
+  }
+  r = wave_max_u32(r);
+  __syncthreads();                                // red[] is free again
+  if (lane == 0) red[wave] = r;
+  __syncthreads();
+  uint32_t amax_bits = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) amax_bits = amax_bits > red[w] ? amax_bits : red[w];
+
+  // 3. scales, the encode factors, then encode from registers and LDS
+  if (amax_bits >= 0x7F800000u) {                // Inf or NaN in the input
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      *tensor_scale = __uint_as_float(0x7FC00000u);
+      if (dev_status) *dev_status = -8;           // NVFP4_ERR_NONFINITE
+    }
+    return;
+  }
+  bool degenerate;
+  float s_enc, s_dec;
+  tensor_scales(__uint_as_float(amax_bits), degenerate, s_enc, s_dec);
+  if (threadIdx.x < 128) e_of[threadIdx.x] = encode_factor(threadIdx.x, s_dec);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *tensor_scale = s_dec;
+    if (dev_status) *dev_status = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const uint32_t blk = lo + (uint32_t)(k * T) + threadIdx.x;
+    if (blk < end) {
+      const float a_b = bf16_bits_to_f32((bm[k / 2] >> (16 * (k % 2))) & 0xFFFFu);
+      u32x2 c;
+      uint32_t S;
+      quantize_block_tab(a[k], b[k], a_b, degenerate, s_enc, e_of, c, S);
+      __builtin_nontemporal_store(c, codes + blk);
+      __builtin_nontemporal_store((uint8_t)S, scales + blk);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < L; ++s) {
+    const int k = R + s;
+    const uint32_t blk = lo + (uint32_t)(k * T + wave * 64 + lane);
+    if (blk < end) {
+      const float a_b = bf16_bits_to_f32((bm[k / 2] >> (16 * (k % 2))) & 0xFFFFu);
+      u32x2 c;
+      uint32_t S;
+      quantize_block_tab(stage[wave][s][2 * lane], stage[wave][s][2 * lane + 1], a_b, degenerate,
+                         s_enc, e_of, c, S);
+      __builtin_nontemporal_store(c, codes + blk);
+      __builtin_nontemporal_store((uint8_t)S, scales + blk);
+    }
   }
 }
 
@@ -190,13 +414,45 @@ int amax_partial_count(int64_t numel) {
   return grid_for(numel / 8, 8, kMaxAmaxPartials);
 }
 
+// The single-pass kernel is used when the amax is computed here, the tensor
+// fits on chip (at most units * (R + L) * 1024 blocks of 16: 109 MB of bf16 on
+// 256 compute units), it is at least kResMinElems elements (below that the
+// two launches of the two-pass kernels cost no more: both are about 15 us
+// there), and the workspace holds the counters, the flags and one partial per
+// compute unit.  NVFP4_QUANT_KERNEL=twopass turns it off, =resident lifts the
+// size floor.
+static constexpr int64_t kResMinElems = (int64_t)3 << 23;   // 25.2 M elements
+
+static bool try_resident(const u32x4* xv, int64_t nblocks, u32x2* codes, uint8_t* scales,
+                         float* tensor_scale, uint32_t* workspace, size_t workspace_bytes,
+                         int32_t* dev_status, hipStream_t stream) {
+  const char* env = getenv("NVFP4_QUANT_KERNEL");
+  const bool forced = env && strcmp(env, "resident") == 0;
+  if (env && strcmp(env, "twopass") == 0) return false;
+  if (!forced && nblocks * 16 < kResMinElems) return false;
+  const int units = compute_units();
+  if (nblocks > (int64_t)units * (kResR + kResL) * kResThreads) return false;
+  if (workspace_bytes < 4u * (size_t)(kResPartials + units)) return false;
+  hipLaunchKernelGGL(clear_sync_kernel, dim3(1), dim3(256), 0, stream, workspace);
+  if (hipGetLastError() != hipSuccess) return false;
+  uint32_t nb = (uint32_t)nblocks;
+  uint32_t chunk = (uint32_t)((nblocks + units - 1) / units);
+  hipLaunchKernelGGL(quantize_resident_kernel, dim3(units), dim3(kResThreads), 0, stream, xv, nb,
+                     chunk, codes, scales, tensor_scale, dev_status, workspace);
+  return true;
+}
+
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, float* tensor_scale, const float* amax_in,
-                           uint32_t* workspace, int32_t* dev_status, hipStream_t stream) {
+                           uint32_t* workspace, size_t workspace_bytes, int32_t* dev_status,
+                           hipStream_t stream) {
   const QuantShape qs = quant_shape();
   const int64_t numel = rows * cols;
   const int64_t nblocks = numel / 16;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  if (!amax_in && try_resident(xv, nblocks, reinterpret_cast<u32x2*>(codes), scales, tensor_scale,
+                               workspace, workspace_bytes, dev_status, stream))
+    return hipGetLastError();
   const uint32_t* words;
   int n_words;
   if (amax_in) {

@@ -9,6 +9,9 @@ calls the kernels' own device helpers).
   * E2M1 decode to fp16 and fp32, and E4M3 decode to fp16 (hardware pair
     conversion) and fp32 (integer decoder): every byte value in every byte
     position of a word.
+  * The single-pass quantizer's block-scale path: a / 6 against IEEE binary32
+    division, the scale byte against the oracle's E4M3 encode, and the codes
+    of a zero-scale block, on every bf16 pattern.
 """
 
 import ctypes
@@ -39,6 +42,7 @@ def probe():
     lib.nvfp4_probe_encode.argtypes = [I, P, I, P, P]
     lib.nvfp4_probe_decode.argtypes = [P, P, I, P, P, P, P, P]
     lib.nvfp4_probe_bf16_gelu.argtypes = [P, I, P, P, P]
+    lib.nvfp4_probe_block_scale.argtypes = [P, I, ctypes.c_float, P, P, P, P]
     return lib
 
 
@@ -230,3 +234,29 @@ def test_gelu_matches_oracle(probe):
     assert rel[near & big].max() < 5e-6, rel[near & big].max()
     assert rel[big].max() < 5e-5, rel[big].max()
     assert np.all(np.abs(g[~big]) <= 1e-30)
+
+
+@pytest.mark.parametrize("s_enc", [1.0, 2688.0 / 3.0, 2688.0 / 0.0123, 2688.0 / 6e4, 2688.0 / 3e-30, 1e30])
+def test_block_scale_path_every_bf16(probe, s_enc):
+    import torch
+    h = np.arange(1 << 16, dtype=np.uint32)
+    b = torch.from_numpy(h.view(np.int32)).cuda()
+    quot = torch.zeros(h.size, dtype=torch.float32, device="cuda")
+    scale = torch.zeros(h.size, dtype=torch.int32, device="cuda")
+    zc = torch.zeros(h.size, dtype=torch.int32, device="cuda")
+    s = np.float32(s_enc)
+    assert probe.nvfp4_probe_block_scale(b.data_ptr(), h.size, float(s), quot.data_ptr(),
+                                         scale.data_ptr(), zc.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    a = ((h & 0x7FFF) << 16).view(np.float32)
+    finite = (h & 0x7FFF) < 0x7F80
+    with np.errstate(invalid="ignore"):
+        want_q = a / np.float32(6.0)                  # IEEE binary32 division
+    got_q = quot.cpu().numpy()
+    assert np.array_equal(got_q[finite].view(np.uint32), want_q[finite].view(np.uint32))
+    with np.errstate(over="ignore"):
+        t = (want_q * s).astype(np.float32)
+    want_s = e4m3_encode_nonneg(t[finite])
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32)[finite], want_s.astype(np.uint32))
+    want_z = np.where(h >> 15, 0x88888888, 0).astype(np.uint32)   # sign-only codes
+    assert np.array_equal(zc.cpu().numpy().view(np.uint32)[finite], want_z[finite])

@@ -75,9 +75,20 @@ SHAPES = [(1, 16), (3, 48), (37, 1040), (257, 3072), (5, 12288)]
 KINDS = ["normal", "t3", "outliers"]
 
 
+# The dynamic-amax quantizer has two implementations: the single-pass kernel
+# that holds the tensor on chip (the default for large tensors that fit) and
+# the two-pass amax + encode kernels (small tensors, larger ones, graph
+# capture).  "resident" forces the first on small shapes, "twopass" the second.
+@pytest.fixture(params=["default", "resident"])
+def quant_kernel(request, monkeypatch):
+    if request.param != "default":
+        monkeypatch.setenv("NVFP4_QUANT_KERNEL", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("kind", KINDS)
-def test_quantize_ragged_shapes(shape, kind):
+def test_quantize_ragged_shapes(shape, kind, quant_kernel):
     bits = W.random_matrix(1000 * SHAPES.index(shape) + KINDS.index(kind), shape, kind)
     q, ref = check_quantize(bits, label=f"{shape} {kind}")
     y = nv.dequantize(q)
@@ -99,6 +110,38 @@ def test_quantize_activation_full_size():
     y = nv.dequantize(q)
     _sync()
     assert np.array_equal(bits_of(y), o_dequantize(ref.codes, ref.scales, ref.tensor_scale, 3072))
+
+
+def test_quantize_activation_full_size_two_pass(monkeypatch):
+    # the same tensor through the two-pass kernels (the default there is the
+    # single-pass one): the same bytes
+    monkeypatch.setenv("NVFP4_QUANT_KERNEL", "twopass")
+    bits = W.quantize_act()["x"]
+    check_quantize(bits, label="act [16896,3072] two-pass")
+
+
+@pytest.mark.parametrize("extra_rows", [0, 1])
+def test_quantize_single_pass_capacity_edge(extra_rows):
+    # the largest tensor of 3072 columns the single-pass kernel holds on chip
+    # (units * 13 * 1024 blocks of 16), and one row more, which goes through
+    # the two-pass kernels; sampled rows against the oracle given the exact
+    # tensor amax, including the rows where one workgroup's range ends
+    import torch
+    units = torch.cuda.get_device_properties(0).multi_processor_count
+    cap_blocks = units * 13 * 1024
+    rows = cap_blocks * 16 // 3072 + extra_rows
+    bits = W.random_matrix(31 + extra_rows, (rows, 3072), "outliers")
+    q = gpu_quantize(bits)
+    amax = np.float32(np.abs(bf16_bits_to_f32(bits)).max())
+    nblocks = rows * 3072 // 16
+    chunk = -(-nblocks // units)
+    edges = [min(rows - 1, (g * chunk * 16) // 3072 + d) for g in (1, units // 2, units - 1) for d in (-1, 0)]
+    rng = np.random.default_rng(extra_rows)
+    sample = np.unique(np.concatenate([[0, rows - 1], edges, rng.choice(rows, 40, replace=False)]))
+    ref = o_quantize(bits[sample], amax=amax)
+    assert np.array_equal(q.scales.cpu().numpy()[sample], ref.scales), "scales"
+    assert np.array_equal(q.codes.cpu().numpy()[sample], ref.codes), "codes"
+    assert q.tensor_scale.cpu().numpy().view(np.uint32)[0] == np.float32(ref.tensor_scale).view(np.uint32)
 
 
 @functools.lru_cache(maxsize=None)
@@ -127,7 +170,7 @@ def _adversarial(seed=0):
     return W.f32_to_bf16_bits(x)
 
 
-def test_quantize_adversarial():
+def test_quantize_adversarial(quant_kernel):
     bits = _adversarial()
     q, ref = check_quantize(bits, label="adversarial")
     y = nv.dequantize(q)
@@ -136,7 +179,7 @@ def test_quantize_adversarial():
     assert (ref.scales == 0).any() and ((ref.scales > 0) & (ref.scales < 8)).any()
 
 
-def test_quantize_exact_e2m1_ties():
+def test_quantize_exact_e2m1_ties(quant_kernel):
     # amax = 2688 makes s_enc = s_dec = 1; a block with max 6 gets scale 1.0, so
     # the elements reach the E2M1 encoder unscaled and sit exactly on its ties
     x = np.zeros((4, 32), np.float32)
@@ -150,7 +193,7 @@ def test_quantize_exact_e2m1_ties():
     assert ref.tensor_scale == np.float32(1.0) and ref.scales[1, 0] == 0x38   # 1.0
 
 
-def test_quantize_degenerate():
+def test_quantize_degenerate(quant_kernel):
     for fill in (0.0, -0.0, 1e-38):
         bits = W.f32_to_bf16_bits(np.full((4, 32), fill, np.float32))
         check_quantize(bits, label=f"fill {fill}")
@@ -163,7 +206,7 @@ def test_quantize_with_producer_amax():
     check_quantize(bits, amax=np.float32(amax * 3.0), label="amax larger")
 
 
-def test_quantize_nonfinite_reports_status():
+def test_quantize_nonfinite_reports_status(quant_kernel):
     import torch
     for bad in (np.inf, -np.inf, np.nan):
         x = np.ones((8, 64), np.float32)
@@ -187,7 +230,7 @@ def test_quantize_empty_rows():
     assert q.codes.shape == (0, 32)
 
 
-def test_quantize_deterministic():
+def test_quantize_deterministic(quant_kernel):
     bits = W.random_matrix(9, (1000, 3072), "outliers")
     x = to_dev(bits)
     a = nv.quantize(x)
