@@ -261,6 +261,7 @@ def main():
                  "GBps_weight_read": round(6 * HIDDEN * HIDDEN * 2 / mod_us / 1e3, 1)}
 
     graphs = None if args.no_graphs or args.no_extras else graph_section(to_dev, ev, stream)
+    shapes = None if args.no_extras else shapes_section(to_dev, ev, stream)
 
     # ----------------------------------------------------------- CPU oracle --
     cpu = None
@@ -287,6 +288,7 @@ def main():
         "static_scale": static,
         "fp8_rowwise": fp8,
         "graphs": graphs,
+        "dit_linear_shapes": shapes,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
     }
@@ -392,6 +394,54 @@ def yardstick_section(c):
         out[name] = {"shape": [m, n, k], "us": st["mm"], "TFLOPs": round(flop / (st["mm"] * 1e-6) / 1e12, 1)}
         del a, w, y
     return {"what": "hipBLASLt fp16 GEMM (torch.matmul), same shapes, no decode or epilogue", **out}
+
+
+def shapes_section(to_dev, ev, stream):
+    """The DiT linears at other real shapes, each GEMM and its dynamic quantize
+    of X timed on its own: the QKV projection at 1024^2 (4608 tokens), and one
+    GPU's share of every linear when the 2048^2 block is split over 8 GPUs by
+    tokens: 4224 tokens (CFG 2 x Ulysses 4 over 33792) and 2112 (Ulysses 8
+    over 16896).  Weights ~ 0.02 N(0,1), quantized once; X ~ N(0,1)."""
+    import torch
+    import nvfp4_block_scaled_05_amd as nv
+    from nvfp4_block_scaled_05_amd import inputs
+
+    def per_call_us(fn, iters=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters
+
+    wshape = {"qkv": (3 * HIDDEN, HIDDEN), "o": (HIDDEN, HIDDEN), "up": (MLP, HIDDEN),
+              "down": (HIDDEN, MLP)}
+    wq = {k: nv.quantize_weight(to_dev(inputs.random_matrix(90 + i, shp, std=0.02)))
+          for i, (k, shp) in enumerate(wshape.items())}
+    cases = [("qkv_1024x1024_cfg2", "qkv", 4608)]
+    cases += [(f"{tag}_{k}", k, m) for tag, m in (("share_of_8_cfg2_ulysses4", 33792 // 8),
+                                                 ("share_of_8_ulysses8", TOKENS // 8))
+              for k in ("qkv", "o", "up", "down")]
+    out = {}
+    for name, k, M in cases:
+        N, K = wshape[k]
+        x = to_dev(inputs.random_matrix(100 + M + N, (M, K)))
+        qx = nv.quantize(x)
+        qws = torch.empty(nv.quantize_workspace_bytes(M, K), dtype=torch.uint8, device=x.device)
+        ws = nv.gemm_workspace(M, N, K, device=x.device)
+        epi = "gelu" if k == "up" else "none"
+        y = nv.gemm(qx, wq[k], epilogue=epi, workspace=ws)
+        q_us = per_call_us(lambda: nv.quantize(x, workspace=qws, out=(qx.codes, qx.scales, qx.tensor_scale)))
+        g_us = per_call_us(lambda: nv.gemm(qx, wq[k], epilogue=epi, out=y, workspace=ws))
+        out[name] = {"M": M, "N": N, "K": K, "epilogue": epi, "quantize_x_us": round(q_us, 2),
+                     "gemm_us": round(g_us, 2),
+                     "gemm_TFLOPs": round(2 * M * N * K / (g_us * 1e-6) / 1e12, 1)}
+        del x, qx, y, ws
+    return out
 
 
 def graph_section(to_dev, ev, stream):

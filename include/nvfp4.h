@@ -162,6 +162,8 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
  *   y_amax            optional device float: set to max |Y| over the bf16
  *                     outputs (the call zeroes it first, on `stream`), ready
  *                     to be passed as amax_in of the next nvfp4_quantize.
+ *                     A NaN output makes it non-finite, which that quantize
+ *                     then reports as NVFP4_ERR_NONFINITE.
  *   workspace         optional device scratch, 256-byte aligned, owned by the
  *                     call until it completes on `stream`; contents on entry
  *                     irrelevant.  With at least nvfp4_gemm_workspace_bytes

@@ -74,27 +74,32 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
 }
 
 // erf-form GELU, z * Phi(z) with Phi(z) = erfc(-z / sqrt 2) / 2.  With
-// x = |z| / sqrt 2 and t = 1 / (1 + |z| / (2 sqrt 2)), erfc(x) / 2 is
-// t * 2^(Q(t) - 1 - z^2 log2(e) / 2), Q a degree-7 polynomial fitted to
-// log2(erfcx(x) / t) on |z| <= 14 (fractional error of erfc below 7e-7;
-// gelu_fit.py beside this file derives the coefficients; the constant term
-// below includes the -1).  The result is accurate relative to |GELU(z)| in
-// both tails; what remains is a few binary32 ulps from the approximate
-// reciprocal and exponential and, far in the negative tail, the rounding of
-// the exponent's argument.
+// x = |z| / sqrt 2 and t = 1 / (1 + |z| / (2 sqrt 2)), h = Phi(-|z|) =
+// erfc(x) / 2 is t * 2^(Q(t) - 1 - z^2 log2(e) / 2), Q a degree-5 polynomial
+// fitted to log2(erfcx(x) / t) on |z| <= 14 (fractional error of erfc below
+// 8e-6; gelu_fit.py beside this file derives the coefficients; the constant
+// term below includes the -1).  Then z * Phi(z) = max(z, 0) - |z| * h for
+// either sign, one FMA.  The result is accurate relative to |GELU(z)| in both
+// tails, to about 1e-5 -- hundreds of times below the bf16 rounding the
+// epilogues apply to it.
 __device__ __forceinline__ float gelu_erf(float z) {
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_fabsf(z), 0.353553391f, 1.0f));
-  float q = -0.26468796f;
-  q = __builtin_fmaf(q, t, 1.0576829f);
-  q = __builtin_fmaf(q, t, -1.397297f);
-  q = __builtin_fmaf(q, t, 0.46071547f);
-  q = __builtin_fmaf(q, t, -0.03360385f);
-  q = __builtin_fmaf(q, t, 0.5611624f);
-  q = __builtin_fmaf(q, t, 1.4417965f);
-  q = __builtin_fmaf(q, t, -2.8257694f);
+  const float az = __builtin_fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(az, 0.353553391f, 1.0f));
+  float q = 0.33010265f;
+  q = __builtin_fmaf(q, t, -1.0232246f);
+  q = __builtin_fmaf(q, t, 0.68463063f);
+  q = __builtin_fmaf(q, t, 0.36704522f);
+  q = __builtin_fmaf(q, t, 1.4686911f);
+  q = __builtin_fmaf(q, t, -2.827234f);
   const float arg = __builtin_fmaf(z * -0.72134752f, z, q);
-  const float h = t * __builtin_amdgcn_exp2f(arg);           // erfc(x) / 2 = Phi(-|z|)
-  return z * (z < 0.0f ? h : 1.0f - h);
+  const float h = t * __builtin_amdgcn_exp2f(arg);           // Phi(-|z|)
+  return __builtin_fmaf(-az, h, __builtin_fmaxf(z, 0.0f));
+}
+
+// Running max |bf16| of two packed bf16 values (the output amax), as 16-bit
+// magnitudes: an integer max, so a NaN output makes the amax non-finite.
+__device__ __forceinline__ u16x2 amax_bf16x2(u16x2 m, uint32_t pair) {
+  return max_u16x2(m, abs_halves(pair));
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {

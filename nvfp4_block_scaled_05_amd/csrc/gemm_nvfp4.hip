@@ -245,9 +245,8 @@ __device__ __forceinline__ void main_loop(const Operand& A, const Operand& Wt, i
 }
 
 // Epilogue: acc * sA*sW + bias (one fused multiply-add), optional GELU, bf16
-// round-to-nearest-even, optional max |bf16 y| (one atomic per wave).  The
-// amax is tracked on the binary32 values and rounded once at the end: bf16
-// rounding is monotone, so this equals the max of the rounded outputs.
+// round-to-nearest-even, optional max |bf16 y| (one atomic per workgroup),
+// an integer max of the bf16 magnitudes, so a NaN output makes it non-finite.
 // A lane holds, per 32x32 tile, column (lane % 32) of rows
 // (e/4)*8 + (lane/32)*4 + e%4; rows e, e+1 are packed by one conversion.
 template <class C>
@@ -261,7 +260,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::TM][C::TN], floa
   const int64_t c0 = n0 + wn * C::WN + (lane & 31);
   const bool full = m0 + C::BM <= M && n0 + C::BN <= N && (int64_t)C::BM * N < ((int64_t)1 << 30);
   uint16_t* __restrict__ yt = y + r0 * N + c0;   // this lane's first element
-  float amax = 0.0f;
+  u16x2 amax = {0, 0};
 #pragma unroll
   for (int j = 0; j < C::TN; ++j) {
     const int64_t col = c0 + j * 32;
@@ -283,22 +282,24 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::TM][C::TN], floa
           const uint32_t off = (uint32_t)dr * (uint32_t)N + (uint32_t)(j * 32);
           yt[off] = (uint16_t)pk;
           yt[off + (uint32_t)N] = (uint16_t)(pk >> 16);
-          amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)));
+          amax = amax_bf16x2(amax, pk);
         } else if (col_ok) {
+          uint32_t kept = 0;
           if (r0 + dr < M) {
             y[(r0 + dr) * N + col] = (uint16_t)pk;
-            amax = __builtin_fmaxf(amax, __builtin_fabsf(v0));
+            kept |= 0xFFFFu;
           }
           if (r0 + dr + 1 < M) {
             y[(r0 + dr + 1) * N + col] = (uint16_t)(pk >> 16);
-            amax = __builtin_fmaxf(amax, __builtin_fabsf(v1));
+            kept |= 0xFFFF0000u;
           }
+          amax = amax_bf16x2(amax, pk & kept);
         }
       }
   }
   if (y_amax) {   // one atomic per workgroup
     __shared__ uint32_t wave_amax[C::NT / 64];
-    uint32_t a = (bf16x2_rne(amax, 0.0f) & 0xFFFFu) << 16;
+    uint32_t a = (uint32_t)(amax.x > amax.y ? amax.x : amax.y) << 16;
     a = wave_max_u32(a);
     if (lane == 0) wave_amax[wave] = a;
     __syncthreads();
@@ -688,7 +689,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
 #pragma unroll
   for (int k = 0; k < 4; ++k) bv[k] = (bias && col + k < N) ? bf16_bits_to_f32(bias[col + k]) : 0.0f;
   const float* slices = part + tail * ways * (int64_t)(C::BM * C::BN);
-  float amax = 0.0f;
+  u16x2 amax = {0, 0};
   for (int r = r0; r < r0 + kReduceRows; r += kRowStep) {
     const int64_t row = tm * C::BM + r;
     const f32x4* src = reinterpret_cast<const f32x4*>(slices + r * C::BN + c);
@@ -708,12 +709,12 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
     for (int k = 0; k < 4; ++k)
       if (col + k < N) {
         dst[k] = h[k];
-        amax = __builtin_fmaxf(amax, __builtin_fabsf(v[k]));
+        amax = max_u16x2(amax, u16x2{(unsigned short)(h[k] & 0x7FFFu), 0});
       }
   }
   if (y_amax) {
     __shared__ uint32_t wave_amax[4];
-    uint32_t a = (bf16x2_rne(amax, 0.0f) & 0xFFFFu) << 16;
+    uint32_t a = (uint32_t)(amax.x > amax.y ? amax.x : amax.y) << 16;
     a = wave_max_u32(a);
     if ((threadIdx.x & 63) == 0) wave_amax[threadIdx.x >> 6] = a;
     __syncthreads();
@@ -1004,11 +1005,11 @@ __device__ __forceinline__ float v5_finish(float a, float scale, float b) {
 }
 
 template <int EPI>
-__device__ __forceinline__ float v5_slice_out(const float* st, float scale, f32x4 bv, int64_t row0,
+__device__ __forceinline__ u16x2 v5_slice_out(const float* st, float scale, f32x4 bv, int64_t row0,
                                               int64_t col, int64_t M, int64_t N, bool vec,
                                               uint16_t* __restrict__ y) {
   const int lane = threadIdx.x & 63, c = lane & 31;
-  float amax = 0.0f;
+  u16x2 amax = {0, 0};
 #pragma unroll 4
   for (int it = 0; it < 16; ++it) {
     const int rr = it * 2 + (lane >> 5);
@@ -1020,15 +1021,14 @@ __device__ __forceinline__ float v5_slice_out(const float* st, float scale, f32x
     const int64_t row = row0 + rr;
     if (vec) {
       *reinterpret_cast<u32x2*>(y + row * N + col) = pk;
-      amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
-                                                   __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]))));
+      amax = amax_bf16x2(amax_bf16x2(amax, pk.x), pk.y);
     } else if (row < M) {
       const uint16_t hv[4] = {(uint16_t)pk.x, (uint16_t)(pk.x >> 16), (uint16_t)pk.y, (uint16_t)(pk.y >> 16)};
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         if (col + t < N) {
           y[row * N + col + t] = hv[t];
-          amax = __builtin_fmaxf(amax, __builtin_fabsf(v[t]));
+          amax = max_u16x2(amax, u16x2{(unsigned short)(hv[t] & 0x7FFFu), 0});
         }
     }
   }
@@ -1045,7 +1045,7 @@ __device__ __forceinline__ void v5_epilogue(const f32x16 (&acc)[kVTM][kVTN], flo
                    (reinterpret_cast<uintptr_t>(y) & 7) == 0;
   const int cl = wn * kVWN + (lane & 31) * 4;               // this lane's 4 columns when reading back
   const f32x4 bv = *reinterpret_cast<const f32x4*>(col_bias + cl);
-  float amax = 0.0f;
+  u16x2 amax = {0, 0};
 #pragma unroll
   for (int i = 0; i < kVTM; ++i) {
     // rows i*32 .. i*32+31 of the wave's tile: lane (r, h) holds row r, and
@@ -1061,15 +1061,15 @@ __device__ __forceinline__ void v5_epilogue(const f32x16 (&acc)[kVTM][kVTN], flo
     __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0): the wave's writes landed
     __builtin_amdgcn_wave_barrier();
     const int64_t row0 = m0 + wm * kVWM + i * 32;
-    const float a = epi == 1 ? v5_slice_out<1>(st, scale, bv, row0, n0 + cl, M, N, vec, y)
+    const u16x2 a = epi == 1 ? v5_slice_out<1>(st, scale, bv, row0, n0 + cl, M, N, vec, y)
                              : v5_slice_out<0>(st, scale, bv, row0, n0 + cl, M, N, vec, y);
-    amax = __builtin_fmaxf(amax, a);
+    amax = max_u16x2(amax, a);
     __builtin_amdgcn_s_waitcnt(0xC07F);                     // reads done before the next slice's writes
     __builtin_amdgcn_wave_barrier();
   }
   if (y_amax) {   // one atomic per workgroup
     __shared__ uint32_t wave_amax[kVNT / 64];
-    uint32_t a = (bf16x2_rne(amax, 0.0f) & 0xFFFFu) << 16;
+    uint32_t a = (uint32_t)(amax.x > amax.y ? amax.x : amax.y) << 16;
     a = wave_max_u32(a);
     if (lane == 0) wave_amax[wave] = a;
     __syncthreads();
@@ -1090,7 +1090,7 @@ __device__ __forceinline__ void v5_epilogue(const f32x16 (&acc)[kVTM][kVTN], flo
 template <int EPI>
 __device__ __forceinline__ void v5_slice_quant(const float* st, uint16_t* st16, float scale, f32x4 bv,
                                                int64_t row0, int64_t col_w, int64_t M, int64_t N,
-                                               bool degenerate, float s_enc, float s_dec,
+                                               bool degenerate, float s_enc, const float* e_of,
                                                const Out& out) {
   const int lane = threadIdx.x & 63, c = lane & 31;
 #pragma unroll 4
@@ -1112,7 +1112,8 @@ __device__ __forceinline__ void v5_slice_quant(const float* st, uint16_t* st16, 
     const u32x4* src = reinterpret_cast<const u32x4*>(st16 + rr * 136 + blk * 16);
     u32x2 cw;
     uint32_t S;
-    quantize_block(src[0], src[1], degenerate, s_enc, s_dec, cw, S);
+    quantize_block_tab(src[0], src[1], bf16_bits_to_f32(block_max_bits(src[0], src[1])), degenerate,
+                       s_enc, e_of, cw, S);
     if (row < M && col < N) {
       *reinterpret_cast<u32x2*>(out.codes + row * code_pitch + col / 2) = cw;
       out.scales[row * scale_pitch + col / 16] = (uint8_t)S;
@@ -1123,7 +1124,7 @@ __device__ __forceinline__ void v5_slice_quant(const float* st, uint16_t* st16, 
 __device__ __forceinline__ void v5_epilogue_quant(const f32x16 (&acc)[kVTM][kVTN], float scale,
                                                   const float* col_bias, int epi, int64_t M,
                                                   int64_t N, int64_t m0, int64_t n0, const Out& out,
-                                                  float* st, uint16_t* st16) {
+                                                  float* st, uint16_t* st16, float* e_of) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, r = lane & 31, h = lane >> 5;
   // tensor scales as the quantizer derives them from a given amax
@@ -1136,6 +1137,9 @@ __device__ __forceinline__ void v5_epilogue_quant(const f32x16 (&acc)[kVTM][kVTN
   float s_enc, s_dec;
   tensor_scales(__uint_as_float(amax_bits), degenerate, s_enc, s_dec);
   if (blockIdx.x == 0 && threadIdx.x == 0) *out.tensor_scale = s_dec;
+  // the wave's table of encode factors (visible after the first slice's wait)
+  e_of[lane] = encode_factor(lane, s_dec);
+  e_of[lane + 64] = encode_factor(lane + 64, s_dec);
   const f32x4 bv = *reinterpret_cast<const f32x4*>(col_bias + wn * kVWN + (lane & 31) * 4);
 #pragma unroll
   for (int i = 0; i < kVTM; ++i) {
@@ -1151,9 +1155,9 @@ __device__ __forceinline__ void v5_epilogue_quant(const f32x16 (&acc)[kVTM][kVTN
     __builtin_amdgcn_wave_barrier();
     const int64_t row0 = m0 + wm * kVWM + i * 32, col_w = n0 + wn * kVWN;
     if (epi == 1)
-      v5_slice_quant<1>(st, st16, scale, bv, row0, col_w, M, N, degenerate, s_enc, s_dec, out);
+      v5_slice_quant<1>(st, st16, scale, bv, row0, col_w, M, N, degenerate, s_enc, e_of, out);
     else
-      v5_slice_quant<0>(st, st16, scale, bv, row0, col_w, M, N, degenerate, s_enc, s_dec, out);
+      v5_slice_quant<0>(st, st16, scale, bv, row0, col_w, M, N, degenerate, s_enc, e_of, out);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_wave_barrier();
   }
@@ -1170,6 +1174,8 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
     SplitK sk) {
   // three stage slots: the loads of stage t + 2 are issued while stage t runs
   __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * kVStage];
+  static_assert(4 * 16384 + 4 * 32 * 136 * 2 + 4 * 512 <= 3 * kVStage,
+                "epilogue staging and encode-factor tables fit in the stage ring");
   __shared__ __attribute__((aligned(16))) float col_bias[kVBN];
   const int64_t tiles_m = (M + kVBM - 1) / kVBM, tiles_n = (N + kVBN - 1) / kVBN;
   int64_t tm, tn, tail;
@@ -1242,7 +1248,8 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
   float* st = reinterpret_cast<float*>(lds + wave * 16384);
   if (kQuant)   // bf16 staging after the four fp32 areas: 32 rows of 136 halves per wave
     v5_epilogue_quant(acc, (*sa) * (*sw), col_bias, epi, M, N, m0, n0, out, st,
-                      reinterpret_cast<uint16_t*>(lds + 4 * 16384 + wave * 32 * 136 * 2));
+                      reinterpret_cast<uint16_t*>(lds + 4 * 16384 + wave * 32 * 136 * 2),
+                      reinterpret_cast<float*>(lds + 4 * 16384 + 4 * 32 * 136 * 2 + wave * 512));
   else
     v5_epilogue(acc, (*sa) * (*sw), col_bias, epi, M, N, m0, n0, out.y, out.y_amax, st);
 }
@@ -1266,7 +1273,7 @@ __global__ __launch_bounds__(256) void v5_split_reduce_kernel(
   grouped_tile(main_tiles + tail, tiles_m, tiles_n, tm, tn);
   const float scale = (*sa) * (*sw);
   const f32x4* slices = reinterpret_cast<const f32x4*>(part) + tail * ways * (int64_t)kQuads;
-  float amax = 0.0f;
+  u16x2 amax = {0, 0};
   for (int q = (int)(blockIdx.x % kV5ReduceWgs) * kPerWg + threadIdx.x;
        q < (int)(blockIdx.x % kV5ReduceWgs + 1) * kPerWg; q += 256) {
     // q = (((wave * 4 + i) * 4 + j) * 64 + lane) * 4 + g
@@ -1291,12 +1298,12 @@ __global__ __launch_bounds__(256) void v5_split_reduce_kernel(
     for (int k = 0; k < 4; ++k)
       if (col + k < N) {
         dst[k] = hv[k];
-        amax = __builtin_fmaxf(amax, __builtin_fabsf(v[k]));
+        amax = max_u16x2(amax, u16x2{(unsigned short)(hv[k] & 0x7FFFu), 0});
       }
   }
   if (y_amax) {
     __shared__ uint32_t wave_amax[4];
-    uint32_t a = (bf16x2_rne(amax, 0.0f) & 0xFFFFu) << 16;
+    uint32_t a = (uint32_t)(amax.x > amax.y ? amax.x : amax.y) << 16;
     a = wave_max_u32(a);
     if ((threadIdx.x & 63) == 0) wave_amax[threadIdx.x >> 6] = a;
     __syncthreads();

@@ -224,14 +224,15 @@ def test_gelu_matches_oracle(probe):
     z = z.astype(np.float32)
     _, g = _bf16_gelu(probe, z)
     ref = gelu_f64(z.astype(np.float64))
-    # relative error well below a bf16 ulp (2^-8): ~1e-6 where exp's argument is
-    # small (a few binary32 ulps of the reciprocal, the Horner steps and exp2); in the
-    # far tail binary32 rounding of x^2 and of the exponent
-    # argument (|arg| up to 800 at |z| = 40) limits it to a few 1e-5
+    # relative error far below a bf16 ulp (2^-8 = 3.9e-3; the epilogues round
+    # GELU to bf16): the degree-5 fit of erfc is good to 8e-6, plus a few
+    # binary32 ulps of the reciprocal, the Horner steps and exp2; in the far
+    # tail binary32 rounding of x^2 and of the exponent argument (|arg| up to
+    # 800 at |z| = 40) adds a few 1e-6
     big = np.abs(ref) > 1e-30
     rel = np.abs(g - ref) / np.where(big, np.abs(ref), 1.0)
     near = np.abs(z) <= 4
-    assert rel[near & big].max() < 5e-6, rel[near & big].max()
+    assert rel[near & big].max() < 2e-5, rel[near & big].max()
     assert rel[big].max() < 5e-5, rel[big].max()
     assert np.all(np.abs(g[~big]) <= 1e-30)
 
