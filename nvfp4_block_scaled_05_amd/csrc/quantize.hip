@@ -137,29 +137,43 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
   }
 }
 
-// Dequantize: y = bf16_rne((value * S) * s_dec); one thread per 16-block per
-// round: one 8-byte code load, one scale byte, two streaming 16-byte stores.
+// Dequantize: y = bf16_rne((value * S) * s_dec).  One lane per 8 elements
+// (half a block): a 4-byte code load, its block's scale byte (shared by the
+// lane pair), one 16-byte streaming store, so each wave instruction writes
+// 1 KB contiguous; two half-blocks per lane per round keep more in flight.
 // The products are binary32 (the first is exact); the packed conversion
 // rounds to nearest-even.
+static constexpr int kDequantU = 2;
+
 __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
-    const u32x2* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ tensor_scale, int64_t nblocks, u32x4* __restrict__ y) {
+    const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const float* __restrict__ tensor_scale, int64_t nhalves, u32x4* __restrict__ y) {
   const float s_dec = *tensor_scale;
-  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; b < nblocks; b += stride) {
-    const u32x2 c = __builtin_nontemporal_load(codes + b);
-    const float S = e4m3_to_f32(scales[b]);
-    uint32_t out[8];
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads * kDequantU;
+  for (int64_t h0 = (int64_t)blockIdx.x * kQuantThreads * kDequantU + threadIdx.x; h0 < nhalves;
+       h0 += stride) {
+    uint32_t w[kDequantU], sb[kDequantU];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t w = h ? c.y : c.x;
-      const f32x2 p[4] = {e2m1_unpack2_f32<0>(w), e2m1_unpack2_f32<1>(w), e2m1_unpack2_f32<2>(w),
-                          e2m1_unpack2_f32<3>(w)};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) out[4 * h + j] = bf16x2_rne((p[j].x * S) * s_dec, (p[j].y * S) * s_dec);
+    for (int u = 0; u < kDequantU; ++u) {
+      const int64_t h = h0 + u * kQuantThreads;
+      if (h < nhalves) {
+        w[u] = __builtin_nontemporal_load(codes + h);
+        sb[u] = scales[h >> 1];
+      }
     }
-    __builtin_nontemporal_store(u32x4{out[0], out[1], out[2], out[3]}, y + 2 * b);
-    __builtin_nontemporal_store(u32x4{out[4], out[5], out[6], out[7]}, y + 2 * b + 1);
+#pragma unroll
+    for (int u = 0; u < kDequantU; ++u) {
+      const int64_t h = h0 + u * kQuantThreads;
+      if (h < nhalves) {
+        const float S = e4m3_to_f32(sb[u]);
+        const f32x2 p[4] = {e2m1_unpack2_f32<0>(w[u]), e2m1_unpack2_f32<1>(w[u]),
+                            e2m1_unpack2_f32<2>(w[u]), e2m1_unpack2_f32<3>(w[u])};
+        uint32_t out[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = bf16x2_rne((p[j].x * S) * s_dec, (p[j].y * S) * s_dec);
+        __builtin_nontemporal_store(u32x4{out[0], out[1], out[2], out[3]}, y + h);
+      }
+    }
   }
 }
 
@@ -491,10 +505,10 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* c
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                              int64_t rows, int64_t cols, void* y, hipStream_t stream) {
-  const int64_t nblocks = rows * cols / 16;
-  const int g = grid_for(nblocks, 4, 8192);
+  const int64_t nhalves = rows * cols / 8;
+  const int g = grid_for(nhalves, kDequantU, 16384);
   hipLaunchKernelGGL(dequantize_kernel, dim3(g), dim3(kQuantThreads), 0, stream,
-                     reinterpret_cast<const u32x2*>(codes), scales, tensor_scale, nblocks,
+                     reinterpret_cast<const uint32_t*>(codes), scales, tensor_scale, nhalves,
                      reinterpret_cast<u32x4*>(y));
   return hipGetLastError();
 }
