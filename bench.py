@@ -3,9 +3,10 @@
 One step = the DiT MLP at 2048x2048 (16384 image + 512 text tokens, hidden
 3072, MLP 12288) as an NVFP4 model runs it:
 
-    quantize(X)                      amax pass + block quantizer   (X bf16 [16896,3072])
+    quantize(X)                      single-pass quantizer          (X bf16 [16896,3072])
+                                     (dynamic amax agreed on chip)
     H = gemm(Xq, Wup_q, GELU, amax)  block-scaled W4A4 GEMM         (16896 x 12288 x 3072)
-    quantize(H, amax)                single-pass quantizer          (H bf16 [16896,12288])
+    quantize(H, amax)                quantizer, producer's amax     (H bf16 [16896,12288])
     Y = gemm(Hq, Wdown_q)            block-scaled W4A4 GEMM         (16896 x 3072 x 12288)
 
 The weights are quantized once before timing (load-time weight quantization),
