@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
 // launched cooperatively (that launch path costs tens of microseconds), so
 // nothing guarantees that all workgroups are resident together: another
 // stream's kernels may hold compute units.  The wait is therefore bounded in
-// time: a workgroup that has not been released after kResWaitTicks reads the
+// time: a workgroup that has not been released after wait_ticks reads the
 // whole tensor for its amax itself (slow, but the same value), so the kernel
 // always completes and always gives the same bytes.
 static constexpr int kResThreads = 1024;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256) void clear_sync_kernel(uint32_t* p) {
 __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(
     const u32x4* __restrict__ x, uint32_t nblocks, uint32_t chunk, u32x2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tensor_scale, int32_t* __restrict__ dev_status,
-    uint32_t* __restrict__ sync) {
+    uint32_t* __restrict__ sync, uint64_t wait_ticks) {
   constexpr int T = kResThreads, NW = T / 64, R = kResR, L = kResL;
   __shared__ u32x4 stage[NW][L][128];   // wave w, slot s: 64 blocks = 128 words
   __shared__ float e_of[128];           // encode factor of every scale byte
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(
     bool ok = true;
     while (__hip_atomic_load(sync + kResGroupFlag + kResLine * grp, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kResWaitTicks) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > wait_ticks) {
         ok = false;
         break;
       }
@@ -451,8 +451,12 @@ static bool try_resident(const u32x4* xv, int64_t nblocks, u32x2* codes, uint8_t
   if (hipGetLastError() != hipSuccess) return false;
   uint32_t nb = (uint32_t)nblocks;
   uint32_t chunk = (uint32_t)((nblocks + units - 1) / units);
+  // NVFP4_QUANT_WAIT_TICKS shortens the wait (tests: 0 sends most
+  // workgroups down the read-everything path)
+  uint64_t wait_ticks = kResWaitTicks;
+  if (const char* w = getenv("NVFP4_QUANT_WAIT_TICKS")) wait_ticks = strtoull(w, nullptr, 10);
   hipLaunchKernelGGL(quantize_resident_kernel, dim3(units), dim3(kResThreads), 0, stream, xv, nb,
-                     chunk, codes, scales, tensor_scale, dev_status, workspace);
+                     chunk, codes, scales, tensor_scale, dev_status, workspace, wait_ticks);
   return true;
 }
 

@@ -101,3 +101,35 @@ def test_dit_block_graph_replays_equal_eager():
     w_bits = bits_of(weights["w_qkv"])
     ref, _ = gemm_fp64(o_quantize(x_bits), o_quantize(w_bits), x_bits.shape[1])
     assert rel_frobenius(eager["transformer_blocks.0.attn.to_qkv"], ref) <= 2e-3
+
+
+@pytest.mark.parametrize("kernel", ["resident", "twopass"])
+def test_dynamic_quantize_graph_replays(kernel, monkeypatch):
+    """The dynamic-amax quantizer captured and replayed: the single-pass
+    kernel (forced on a small tensor) with its counter-clearing launch, and
+    the two-pass kernels.  Every replay equals the eager bytes and the oracle,
+    with eager quantizes of another tensor on the same workspace between
+    replays (they leave its counters and partials behind)."""
+    import torch
+    monkeypatch.setenv("NVFP4_QUANT_KERNEL", kernel)
+    bits = W.random_matrix(41, (300, 1024), "outliers")
+    x = to_dev(bits)
+    ws = torch.empty((4096,), dtype=torch.uint8, device="cuda")
+    out = (torch.empty((300, 512), dtype=torch.uint8, device="cuda"),
+           torch.empty((300, 64), dtype=torch.uint8, device="cuda"),
+           torch.empty((1,), dtype=torch.float32, device="cuda"))
+    fn = lambda: nv.quantize(x, workspace=ws, out=out)
+    q = fn()
+    _sync()
+    eager = [t.cpu().numpy().copy() for t in (q.codes, q.scales, q.tensor_scale)]
+    ref = o_quantize(bits)
+    assert np.array_equal(eager[0], ref.codes) and np.array_equal(eager[1], ref.scales)
+    g = capture(fn)
+    other = to_dev(W.random_matrix(42, (300, 1024), "t3"))
+    for _ in range(4):
+        nv.quantize(other, workspace=ws)     # eager work on the same workspace
+        _sync()
+        g.replay()
+        _sync()
+        got = [t.cpu().numpy() for t in (out[0], out[1], out[2])]
+        assert all(np.array_equal(a, b) for a, b in zip(got, eager))

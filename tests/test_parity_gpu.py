@@ -564,3 +564,23 @@ def test_linear_dispatch_by_layer_name():
     assert_gemm_close(y_q, ref, "nvfp4 layer")
     y_b = bits_of(nv.linear(x, to_dev(d["w"]), "proj_out"))
     assert_gemm_close(y_b, linear_bf16_fp64(d["x"], d["w"]), "bf16 layer")
+
+
+@pytest.mark.parametrize("shape", [(300, 1024), (16896, 3072)])
+def test_quantize_single_pass_wait_timeout_path(shape, monkeypatch):
+    # a zero wait limit makes every workgroup that is not released at once
+    # read the whole tensor for its amax itself (the path taken when the grid
+    # is not co-resident): the same bytes as the oracle
+    monkeypatch.setenv("NVFP4_QUANT_KERNEL", "resident")
+    monkeypatch.setenv("NVFP4_QUANT_WAIT_TICKS", "0")
+    bits = W.random_matrix(51, shape, "outliers")
+    if shape[0] * shape[1] <= 1 << 20:
+        check_quantize(bits, label=f"{shape} timeout path")
+        return
+    q = gpu_quantize(bits)
+    amax = np.float32(np.abs(bf16_bits_to_f32(bits)).max())
+    rows = np.unique(np.concatenate([[0, shape[0] - 1], np.random.default_rng(3).choice(shape[0], 40, replace=False)]))
+    ref = o_quantize(bits[rows], amax=amax)
+    assert np.array_equal(q.scales.cpu().numpy()[rows], ref.scales)
+    assert np.array_equal(q.codes.cpu().numpy()[rows], ref.codes)
+    assert q.tensor_scale.cpu().numpy().view(np.uint32)[0] == np.float32(ref.tensor_scale).view(np.uint32)
