@@ -58,10 +58,15 @@ def parse():
 
 
 def kernel_source_hash():
+    """Hash of the HIP / C++ sources the library is built from (the counter
+    summary under profiles/ is valid only for the sources it was taken on)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_block_scaled_05_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+        path = os.path.join(csrc, name)
+        if not os.path.isfile(path) or not name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            continue
+        with open(path, "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
