@@ -124,8 +124,10 @@ size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
  * agreed, then encodes it.  The workgroups of that kernel wait for each other; if another
  * stream's work keeps some of them from starting, the waiting ones time out
  * after 200 us and compute the amax themselves, so the call still completes
- * with the same bytes, only slower.  Other sizes take two passes over the
- * input.  NVFP4_QUANT_KERNEL=twopass (environment) forces the two passes.
+ * with the same bytes, only slower.  A tensor of at most 262,144 elements
+ * is quantized in one launch whose workgroups each fold the whole amax
+ * themselves.  Other sizes take two passes over the input.
+ * NVFP4_QUANT_KERNEL=twopass|resident|small (environment) forces a kernel.
  */
 int nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols,
                    uint8_t* codes, uint8_t* scales, float* tensor_scale,

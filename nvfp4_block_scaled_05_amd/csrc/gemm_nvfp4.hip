@@ -1335,16 +1335,28 @@ hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const fl
 
 using CfgPipe = Cfg<256, 256, 4, 2, 1>;    // 8 waves of 64x128 (v3)
 using CfgSmall = Cfg<128, 128, 2, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU (v1)
+using CfgTiny = Cfg<64, 64, 2, 2, 2>;      // 4 waves of 32x32 (v1), for few-tile problems
 
 // DiT-sized problems run v5 (K % 128 == 0, aligned rows) or v3 on 256x256
-// tiles; small ones v1 on 128x128 tiles, two workgroups per CU.
-// NVFP4_GEMM_KERNEL=small|pipe|v5 pins one (testing; v5 only where it applies).
+// tiles; small ones v1 on 128x128 tiles, two workgroups per CU, or on 64x64
+// tiles when 128x128 ones would leave more than half the compute units idle.
+// NVFP4_GEMM_KERNEL=tiny|small|pipe|v5 pins one (testing; v5 only where it
+// applies).
 bool use_pipe(int64_t M, int64_t N) {
   if (const char* f = getenv("NVFP4_GEMM_KERNEL")) {
     if (!strcmp(f, "pipe") || !strcmp(f, "v5")) return true;
-    if (!strcmp(f, "small")) return false;
+    if (!strcmp(f, "small") || !strcmp(f, "tiny")) return false;
   }
   return M * N > (int64_t)256 * 256 * 128;
+}
+
+bool use_tiny(int64_t M, int64_t N) {
+  if (const char* f = getenv("NVFP4_GEMM_KERNEL")) {
+    if (!strcmp(f, "tiny")) return true;
+    if (!strcmp(f, "small")) return false;
+  }
+  const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
+  return 2 * tiles128 < compute_units();
 }
 
 // v5 needs K % 128 == 0, 16-byte aligned code rows, 4-byte aligned scale
@@ -1506,6 +1518,9 @@ hipError_t launch_any(const uint8_t* a_codes, const uint8_t* a_scales, const flo
   if (use_pipe(M, N))
     return launch_pipe(a_codes, a_scales, sa, w_codes, w_scales, sw, bias, M, N, K, epilogue, out,
                        workspace, workspace_bytes, stream);
+  if (use_tiny(M, N))
+    return launch_tile<CfgTiny>(a_codes, a_scales, sa, w_codes, w_scales, sw, bias, M, N, K,
+                                epilogue, out, stream);
   return launch_tile<CfgSmall>(a_codes, a_scales, sa, w_codes, w_scales, sw, bias, M, N, K,
                                epilogue, out, stream);
 }

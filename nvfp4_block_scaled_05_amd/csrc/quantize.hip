@@ -5,10 +5,11 @@
 // from the tensor amax, and one scale per block of 16 elements computed in the
 // same pass that encodes the elements.
 //
-// With the amax computed here, a tensor that fits on chip (up to 109 MB of
-// bf16 on 256 compute units) takes the single-pass kernel further down, which
-// reads it from HBM once; otherwise quantization is two launches, both
-// HBM-bound:
+// With the amax computed here, a small tensor (up to 512 KB of bf16) takes a
+// one-launch kernel whose workgroups each fold the whole amax, and one that
+// fits on chip (up to 109 MB on 256 compute units) the single-pass kernel
+// further down, which reads it from HBM once; otherwise quantization is two
+// launches, both HBM-bound:
 //   amax_partial_kernel  every workgroup reads a grid-strided slice with
 //                        128-bit loads (ordinary loads, so the tensor stays in
 //                        the last-level cache for the second pass) and writes one partial max|x| (as the
@@ -24,6 +25,7 @@
 // The arithmetic is binary32 round-to-nearest-even throughout: divisions are
 // correctly rounded (no fast-math) and the file is built with FP contraction
 // off, so every value equals the CPU oracle's bit for bit.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -132,6 +134,69 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
     u32x2 c;
     uint32_t S;
     quantize_block_tab(lo, hi, bf16_bits_to_f32(block_max_bits(lo, hi)), degenerate, s_enc, e_of, c, S);
+    codes[b] = c;
+    scales[b] = (uint8_t)S;
+  }
+}
+
+// One-launch quantizer for small tensors (at most kSmallMaxElems elements,
+// 512 KB of bf16): every workgroup folds the amax of the whole tensor itself
+// (the first reads come from HBM, the rest mostly from L2), then encodes its
+// own range of blocks.  No workspace, no second launch, no waiting on other
+// workgroups; the same bytes as the other kernels.
+static constexpr int kSmallThreads = 512;
+static constexpr int kSmallMaxGrid = 16;
+static constexpr int64_t kSmallMaxElems = (int64_t)1 << 18;
+
+__global__ __launch_bounds__(kSmallThreads) void quantize_small_kernel(
+    const u32x4* __restrict__ x, uint32_t nblocks, uint32_t chunk, u32x2* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tensor_scale,
+    int32_t* __restrict__ dev_status) {
+  constexpr int NW = kSmallThreads / 64;
+  __shared__ uint32_t red[NW];
+  __shared__ float e_of[128];
+  const uint32_t n16 = 2 * nblocks;
+  u16x2 m = {0, 0};
+  uint32_t w = threadIdx.x;
+  for (; w + 7 * kSmallThreads < n16; w += 8 * kSmallThreads) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = x[w + u * kSmallThreads];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = max_u16x2(m, max8(v[u]));
+  }
+  for (; w < n16; w += kSmallThreads) m = max_u16x2(m, max8(x[w]));
+  const uint32_t r = wave_max_u32(m.x > m.y ? m.x : m.y);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = r;
+  __syncthreads();
+  uint32_t amax16 = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) amax16 = amax16 > red[i] ? amax16 : red[i];
+  const uint32_t amax_bits = amax16 << 16;
+  const bool first = blockIdx.x == 0 && threadIdx.x == 0;
+  if (amax_bits >= 0x7F800000u) {                 // Inf or NaN in the input
+    if (first) {
+      *tensor_scale = __uint_as_float(0x7FC00000u);
+      if (dev_status) *dev_status = -8;           // NVFP4_ERR_NONFINITE
+    }
+    return;
+  }
+  bool degenerate;
+  float s_enc, s_dec;
+  tensor_scales(__uint_as_float(amax_bits), degenerate, s_enc, s_dec);
+  if (first) {
+    *tensor_scale = s_dec;
+    if (dev_status) *dev_status = 0;
+  }
+  if (threadIdx.x < 128) e_of[threadIdx.x] = encode_factor(threadIdx.x, s_dec);
+  __syncthreads();
+  const uint32_t lo = blockIdx.x * chunk;
+  const uint32_t end = lo + chunk < nblocks ? lo + chunk : nblocks;
+  for (uint32_t b = lo + threadIdx.x; b < end; b += kSmallThreads) {
+    const u32x4 v0 = x[2 * b], v1 = x[2 * b + 1];
+    u32x2 c;
+    uint32_t S;
+    quantize_block_tab(v0, v1, bf16_bits_to_f32(block_max_bits(v0, v1)), degenerate, s_enc, e_of, c, S);
     codes[b] = c;
     scales[b] = (uint8_t)S;
   }
@@ -468,6 +533,16 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* c
   const int64_t numel = rows * cols;
   const int64_t nblocks = numel / 16;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  const char* kind = getenv("NVFP4_QUANT_KERNEL");
+  if (!amax_in && (kind ? strcmp(kind, "small") == 0 : numel <= kSmallMaxElems) &&
+      numel <= kSmallMaxElems) {
+    const int g = (int)std::min<int64_t>(kSmallMaxGrid, (nblocks + kSmallThreads - 1) / kSmallThreads);
+    const uint32_t chunk = (uint32_t)((nblocks + g - 1) / g);
+    hipLaunchKernelGGL(quantize_small_kernel, dim3(g), dim3(kSmallThreads), 0, stream, xv,
+                       (uint32_t)nblocks, chunk, reinterpret_cast<u32x2*>(codes), scales,
+                       tensor_scale, dev_status);
+    return hipGetLastError();
+  }
   if (!amax_in && try_resident(xv, nblocks, reinterpret_cast<u32x2*>(codes), scales, tensor_scale,
                                workspace, workspace_bytes, dev_status, stream))
     return hipGetLastError();

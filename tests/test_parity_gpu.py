@@ -75,11 +75,12 @@ SHAPES = [(1, 16), (3, 48), (37, 1040), (257, 3072), (5, 12288)]
 KINDS = ["normal", "t3", "outliers"]
 
 
-# The dynamic-amax quantizer has two implementations: the single-pass kernel
-# that holds the tensor on chip (the default for large tensors that fit) and
-# the two-pass amax + encode kernels (small tensors, larger ones, graph
-# capture).  "resident" forces the first on small shapes, "twopass" the second.
-@pytest.fixture(params=["default", "resident"])
+# The dynamic-amax quantizer has three implementations: the one-launch
+# kernel for small tensors (every workgroup folds the whole amax itself), the
+# single-pass kernel that holds the tensor on chip (large tensors that fit),
+# and the two-pass amax + encode kernels (everything else).  The fixture runs
+# each case through the default choice and through each kernel forced.
+@pytest.fixture(params=["default", "small", "resident", "twopass"])
 def quant_kernel(request, monkeypatch):
     if request.param != "default":
         monkeypatch.setenv("NVFP4_QUANT_KERNEL", request.param)
@@ -381,11 +382,12 @@ def test_gemm_deterministic():
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 520, 1088), (257, 300, 1040), (64, 33, 3072)])
-@pytest.mark.parametrize("kernel,split", [("small", None), ("pipe", None), ("pipe", "3"),
-                                          ("pipe", "7")])
+@pytest.mark.parametrize("kernel,split", [("tiny", None), ("small", None), ("pipe", None),
+                                          ("pipe", "3"), ("pipe", "7")])
 def test_gemm_kernels_and_k_split(monkeypatch, M, N, K, kernel, split):
-    # every kernel path on ragged tiles: 128x128 tiles, 256x256 tiles whole,
-    # and 256x256 tiles with their K range split over 3 or 7 workgroups
+    # every kernel path on ragged tiles: 64x64 and 128x128 tiles, 256x256
+    # tiles whole, and 256x256 tiles with their K range split over 3 or 7
+    # workgroups
     monkeypatch.setenv("NVFP4_GEMM_KERNEL", kernel)
     if split:
         monkeypatch.setenv("NVFP4_GEMM_SPLIT", split)
@@ -473,7 +475,7 @@ def _gemm_quantized_case(M, N, K, seed, amax_factor, epilogue="none", bias=False
 
 @pytest.mark.parametrize("M,N,K", [(300, 528, 1088), (257, 16, 64), (64, 1024, 2048),
                                    (300, 528, 1152), (257, 16, 128)])
-@pytest.mark.parametrize("kernel", ["small", "pipe", "v5"])
+@pytest.mark.parametrize("kernel", ["tiny", "small", "pipe", "v5"])
 def test_gemm_quantized_equals_gemm_then_quantize(monkeypatch, M, N, K, kernel):
     monkeypatch.setenv("NVFP4_GEMM_KERNEL", kernel)
     for factor, epi, bias in ((1.0, "gelu", True), (0.25, "none", False), (8.0, "none", True)):
