@@ -1342,12 +1342,14 @@ using CfgTiny = Cfg<64, 64, 2, 2, 2>;      // 4 waves of 32x32 (v1), for few-til
 // tiles when 128x128 ones would leave more than half the compute units idle.
 // NVFP4_GEMM_KERNEL=tiny|small|pipe|v5 pins one (testing; v5 only where it
 // applies).
-bool use_pipe(int64_t M, int64_t N) {
+bool use_pipe(int64_t M, int64_t N, int64_t K) {
   if (const char* f = getenv("NVFP4_GEMM_KERNEL")) {
     if (!strcmp(f, "pipe") || !strcmp(f, "v5")) return true;
     if (!strcmp(f, "small") || !strcmp(f, "tiny")) return false;
   }
-  return M * N > (int64_t)256 * 256 * 128;
+  // a long K favours the 256x256 kernels and their K split even when the
+  // output is small (2112 x 3072 x 12288: 171 us against 240 on 128x128 tiles)
+  return M * N > (int64_t)256 * 256 * 128 || K >= 8192;
 }
 
 bool use_tiny(int64_t M, int64_t N) {
@@ -1436,6 +1438,27 @@ hipError_t launch_pipe(const uint8_t* a_codes, const uint8_t* a_scales, const fl
 // most 8 ways (each way adds a slice of partial sums to write and read back;
 // the DiT up projection's 96 tail tiles would split only 2 ways, which
 // measured slower than computing them whole).
+// Ways for a grid whose tiles are all tail tiles (fewer tiles than compute
+// units): minimise, in stage times, the rounds over the compute units times
+// the stages per split, plus the split's cost -- each fp32 partial tile
+// (256 KB written and read back, about 0.2 us) and the reduce launch (about
+// 5 us), at about 2.9 us per stage.  A K-heavy grid of 108 tiles (2112 x 3072
+// x 12288) splits 2 ways; grids whose second round would be mostly idle, or
+// whose K is short, stay whole.
+int64_t all_tail_ways(int64_t tiles, int64_t nk, int cus) {
+  int64_t best = 1;
+  double best_cost = (double)nk;
+  for (int64_t w = 2; w <= 8 && w <= nk; ++w) {
+    const int64_t rounds = (tiles * w + cus - 1) / cus;
+    const double cost = (double)(rounds * ((nk + w - 1) / w)) + ((double)(tiles * w) * 0.2 + 5.0) / 2.9;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = w;
+    }
+  }
+  return best;
+}
+
 SplitPlan plan_split_v5(int64_t M, int64_t N, int64_t K) {
   SplitPlan p;
   p.tiles = p.main_tiles = ((M + kVBM - 1) / kVBM) * ((N + kVBN - 1) / kVBN);
@@ -1446,6 +1469,7 @@ SplitPlan plan_split_v5(int64_t M, int64_t N, int64_t K) {
   if (tail == 0) return p;
   int64_t ways = std::min<int64_t>(std::min<int64_t>(cus / tail, nk / 4), 8);
   if (ways < 3) ways = 1;
+  if (p.tiles < cus) ways = all_tail_ways(p.tiles, nk, cus);
   if (const char* f = getenv("NVFP4_GEMM_SPLIT")) ways = std::min<int64_t>(atoi(f), nk);
   if (ways < 2) return p;
   p.tail = tail;
@@ -1492,7 +1516,7 @@ int compute_units() {
 }
 
 size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || !use_pipe(M, N)) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || !use_pipe(M, N, K)) return 0;
   // the plan of the kernel that runs with aligned operands
   return v5_applies(M, N, K, 0, 0) ? plan_split_v5(M, N, K).bytes : plan_split(M, N, K).bytes;
 }
@@ -1512,10 +1536,10 @@ hipError_t launch_any(const uint8_t* a_codes, const uint8_t* a_scales, const flo
   if (M == 0 || N == 0) return hipSuccess;
   const uintptr_t code_bits = reinterpret_cast<uintptr_t>(a_codes) | reinterpret_cast<uintptr_t>(w_codes);
   const uintptr_t scale_bits = reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(w_scales);
-  if (use_pipe(M, N) && v5_applies(M, N, K, code_bits, scale_bits))
+  if (use_pipe(M, N, K) && v5_applies(M, N, K, code_bits, scale_bits))
     return launch_v5(a_codes, a_scales, sa, w_codes, w_scales, sw, bias, M, N, K, epilogue, out,
                      workspace, workspace_bytes, stream);
-  if (use_pipe(M, N))
+  if (use_pipe(M, N, K))
     return launch_pipe(a_codes, a_scales, sa, w_codes, w_scales, sw, bias, M, N, K, epilogue, out,
                        workspace, workspace_bytes, stream);
   if (use_tiny(M, N))
