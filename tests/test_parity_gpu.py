@@ -586,3 +586,33 @@ def test_quantize_single_pass_wait_timeout_path(shape, monkeypatch):
     assert np.array_equal(q.scales.cpu().numpy()[rows], ref.scales)
     assert np.array_equal(q.codes.cpu().numpy()[rows], ref.codes)
     assert q.tensor_scale.cpu().numpy().view(np.uint32)[0] == np.float32(ref.tensor_scale).view(np.uint32)
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 40, 8192), (70, 300, 12288)])
+def test_gemm_long_k_small_output(M, N, K):
+    # a long K sends even a small output to the 256x256 kernel, whose grid of
+    # fewer tiles than compute units takes its K split from the cost model
+    a_bits = W.random_matrix(M + 7 * N, (M, K), "t3")
+    w_bits = W.random_matrix(N + 5 * M, (N, K), "normal", 0.02)
+    qa, ra = check_quantize(a_bits)
+    qw, rw = check_quantize(w_bits)
+    ws = nv.gemm_workspace(M, N, K)
+    assert ws is not None                    # the plan splits
+    y = bits_of(nv.gemm(qa, qw, workspace=ws))
+    ref, _ = gemm_fp64(ra, rw, K)
+    assert_gemm_close(y, ref, f"{M}x{N}x{K}")
+
+
+def test_gemm_share_of_8_down_sampled_rows():
+    # one GPU's share of the MLP down projection when the 2048^2 block is
+    # split over 8 GPUs by tokens: H [2112,12288] x W_down [3072,12288]^T, a
+    # grid of 108 tiles split 2 ways over K; sampled rows against the exact sum
+    M, N, K = 2112, 3072, 12288
+    h_bits = W.random_matrix(81, (M, K), "normal", 0.5)
+    qh, rh = check_quantize(h_bits)
+    wb, rw = _oracle_weight("w_down")
+    qw = gpu_quantize(wb)
+    y = bits_of(nv.gemm(qh, qw, workspace=nv.gemm_workspace(M, N, K)))
+    rows = _sampled_rows(M, 48, seed=5)
+    ref, _ = gemm_exact_rows(rh, rw, K, rows)
+    assert_gemm_close(y[rows], ref, "down share rows")
