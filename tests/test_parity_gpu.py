@@ -616,3 +616,51 @@ def test_gemm_share_of_8_down_sampled_rows():
     rows = _sampled_rows(M, 48, seed=5)
     ref, _ = gemm_exact_rows(rh, rw, K, rows)
     assert_gemm_close(y[rows], ref, "down share rows")
+
+
+def _random_shapes(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(1, 700))
+        N = int(rng.integers(1, 700))
+        K = 16 * int(rng.choice([rng.integers(1, 24), rng.integers(24, 200), 8 * rng.integers(1, 25)]))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes())
+def test_gemm_random_shapes(M, N, K):
+    # seeded random shapes through the default dispatch (64x64, 128x128 or
+    # 256x256 tiles, with or without a K split): bias + GELU against the oracle
+    a_bits = W.random_matrix(M * 31 + K, (M, K), "t3")
+    w_bits = W.random_matrix(N * 17 + K, (N, K), "normal", 0.02)
+    b_bits = W.random_matrix(M + N + K, (1, N), "normal", 0.1)[0]
+    qa, ra = check_quantize(a_bits, label=f"A {M}x{K}")
+    qw, rw = check_quantize(w_bits, label=f"W {N}x{K}")
+    y = bits_of(nv.gemm(qa, qw, bias=to_dev(b_bits), epilogue="gelu",
+                        workspace=nv.gemm_workspace(M, N, K)))
+    ref, _ = gemm_fp64(ra, rw, K, bias_bits=b_bits, gelu=True)
+    assert_gemm_close(y, ref, f"{M}x{N}x{K}")
+
+
+def _random_big_shapes(n=6, seed=77):
+    rng = np.random.default_rng(seed)
+    # even cases: K a multiple of 128 (v5); odd cases: any multiple of 16 (v3)
+    return [(int(rng.integers(2900, 4300)), int(rng.integers(2900, 4300)),
+             128 * int(rng.integers(2, 12)) if i % 2 == 0 else 16 * int(rng.integers(8, 80)))
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("M,N,K", _random_big_shapes())
+def test_gemm_random_large_shapes_sampled_rows(M, N, K):
+    # seeded random shapes large enough for the 256x256 kernels (v5 where
+    # K % 128 == 0, else v3; tail split by the default plan): sampled rows
+    a_bits = W.random_matrix(M + 3 * K, (M, K), "t3")
+    w_bits = W.random_matrix(N + 5 * K, (N, K), "normal", 0.02)
+    qa, ra = check_quantize(a_bits, label=f"A {M}x{K}")
+    qw, rw = check_quantize(w_bits, label=f"W {N}x{K}")
+    y = bits_of(nv.gemm(qa, qw, epilogue="gelu", workspace=nv.gemm_workspace(M, N, K)))
+    rows = _sampled_rows(M, 40, seed=M)
+    ref, _ = gemm_fp64(ra, rw, K, gelu=True, rows=rows)
+    assert_gemm_close(y[rows], ref, f"{M}x{N}x{K}")
