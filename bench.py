@@ -543,7 +543,27 @@ def cpu_baseline(data, rows):
             "sample": f"{rows} of {TOKENS} token rows through the whole step (amax over all of X, "
                       f"quantize, float64-BLAS GEMM up + GELU, quantize H, GEMM down); "
                       f"weights quantized beforehand in {t_w:.1f}s (not counted)",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "host": _host_info(threads)}
+
+
+def _host_info(blas_threads):
+    """The CPU the baseline ran on: model, logical CPUs, the ones this process
+    may use, and the BLAS thread count."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "usable_cpus": usable,
+            "blas_threads": int(blas_threads)}
 
 
 if __name__ == "__main__":
