@@ -179,6 +179,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     stage_us = {n: float(np.mean([s[j].elapsed_time(s[j + 1]) * 1e3 for s in ev_sets]))
                 for j, n in enumerate(stage_names)}
+    step_ev_ms = np.array([s[0].elapsed_time(s[-1]) for s in ev_sets])
+    step_pct = {f"p{q}": round(float(np.percentile(step_ev_ms, q)), 4) for q in (10, 50, 90)}
     value = 2 * GEMM_FLOP / (ms_per_step * 1e-3) / 1e12
 
     extras = SimpleNamespace(x=x, xq=xq, xq_out=xq_out, wq_up=wq_up, wq_down=wq_down, amax=amax,
@@ -286,6 +288,7 @@ def main():
                    "tokens": TOKENS, "hidden": HIDDEN, "mlp": MLP,
                    "flop_per_step": 2 * GEMM_FLOP, "parallelism": "single GPU"},
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "step_ms_events": step_pct,
         "weight_quantize_us": round(wquant_us, 2),
         "roofline": roofline,
         "quantize": quant,
