@@ -7,6 +7,9 @@
 // Tiling: 128x128 output tile per 256-thread workgroup, K step 64, LDS
 // double-buffered with a register prefetch of the next K step; each of the 4
 // waves owns a 64x64 sub-tile = 2x2 v_mfma_f32_32x32x16_bf16 tiles.
+#include <cstdlib>
+#include <cstring>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -158,6 +161,241 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(
   epilogue(acc, 1.0f, bias, epi, M, N, m0, n0, y, nullptr);
 }
 
+// Large problems (256x256 tiles covering at least half the compute units,
+// K % 64 == 0, 16-byte aligned operands): each workgroup computes a 256x256
+// tile with 4 waves of 128x128 (256 fp32 accumulators per lane, in AGPRs at one
+// wave per SIMD).  Operands go from global memory straight into LDS with the
+// gfx950 global->LDS load (lane L's 16 bytes land at offset 16 L of the 1 KB
+// the instruction fills): per stage 64 K, i.e. 128 bytes of bf16 per row, in
+// two separately declared 64 KB buffers, so the compiler sees that a stage's
+// LDS reads do not alias the load in flight into the other buffer.  Inside a
+// 128-byte row the 16-byte pieces are permuted by XOR with (row / 2) % 8: the
+// fragment reads (16 lanes, 16 consecutive rows, one logical piece) then hit
+// distinct bank groups.  v_mfma_f32_32x32x16_bf16 takes one piece per lane and
+// row: k-step s of a stage is piece 2s + h for lane half h.  The weight
+// fragment is the MFMA's first operand, so each lane holds four consecutive
+// columns of one output row, and the epilogue moves 32 rows at a time through
+// LDS to write 8-byte stores.
+constexpr int kEBM = 256, kEBN = 256, kEBK = 64, kENT = 256;
+constexpr int kEWM = 128, kEWN = 128, kETM = 4, kETN = 4;
+constexpr int kERow = kEBK * 2;              // 128 bytes per row and stage
+constexpr int kEOp = kEBM * kERow;           // 32 KB per operand and stage
+constexpr int kEStage = 2 * kEOp;            // A, then W
+
+// This lane's source offsets (bytes from the operand's start; rows * K * 2 <
+// 2^32 is checked on the host), one per 8-row chunk it loads.
+struct BDmaPtrs {
+  uint32_t a[kEBM / 8 / 4];
+  uint32_t w[kEBN / 8 / 4];
+};
+
+__device__ __forceinline__ void bdma_setup(int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                           BDmaPtrs& d) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t pitch = K * 2;
+#pragma unroll
+  for (int i = 0; i < kEBM / 8 / 4; ++i) {
+    const int c = wave * (kEBM / 8 / 4) + i;             // chunk: rows 8c .. 8c+7
+    const int row = 8 * c + (lane >> 3);
+    const int piece = (lane & 7) ^ ((row >> 1) & 7);
+    const int64_t ra = m0 + row < M ? m0 + row : M - 1;
+    const int64_t rw = n0 + row < N ? n0 + row : N - 1;
+    d.a[i] = (uint32_t)(ra * pitch + piece * 16);
+    d.w[i] = (uint32_t)(rw * pitch + piece * 16);
+  }
+}
+
+__device__ __forceinline__ void bdma_issue(const uint8_t* __restrict__ a, const uint8_t* __restrict__ w,
+                                           const BDmaPtrs& d, int64_t kbyte, uint8_t* stage) {
+  const int wave = wave_id();
+  const uint8_t* ak = a + kbyte;
+  const uint8_t* wk = w + kbyte;
+#pragma unroll
+  for (int i = 0; i < kEBM / 8 / 4; ++i) {
+    const int c = wave * (kEBM / 8 / 4) + i;
+    __builtin_amdgcn_global_load_lds(ak + d.a[i], stage + c * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wk + d.w[i], stage + kEOp + c * 1024, 16, 0, 0);
+  }
+}
+
+struct BFrags {
+  u32x4 a[kETM], b[kETN];
+};
+
+// Fragments of k-step S (0..3) of a stage; a_off / b_off: this lane's byte
+// offset of its row in the wave's first A / W tile; sw = (row / 2) % 8.
+template <int S>
+__device__ __forceinline__ void bfrags(const uint8_t* stage, int a_off, int b_off, int h, int sw,
+                                       BFrags& f) {
+  const int p = ((2 * S + h) ^ sw) << 4;
+#pragma unroll
+  for (int i = 0; i < kETM; ++i)
+    f.a[i] = *reinterpret_cast<const u32x4*>(stage + a_off + i * 32 * kERow + p);
+#pragma unroll
+  for (int j = 0; j < kETN; ++j)
+    f.b[j] = *reinterpret_cast<const u32x4*>(stage + kEOp + b_off + j * 32 * kERow + p);
+}
+
+__device__ __forceinline__ void bmfma(const BFrags& f, f32x16 (&acc)[kETM][kETN]) {
+#pragma unroll
+  for (int i = 0; i < kETM; ++i)
+#pragma unroll
+    for (int j = 0; j < kETN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.b[j]),
+                                                          __builtin_bit_cast(bf16x8, f.a[i]),
+                                                          acc[i][j], 0, 0, 0);
+}
+
+// Every load of this wave has landed in LDS (vmcnt 0), then the workgroup
+// barrier: the next stage is visible and all reads of the buffer about to be
+// refilled are done.
+__device__ __forceinline__ void bdma_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// One stage: refill `nxt` with the stage after this one (if any), read this
+// stage's four k-steps from `cur` and run the previous stage's last k-step
+// and this stage's first three, MFMAs interleaved with the reads and loads.
+__device__ __forceinline__ void bdma_stage(const uint8_t* __restrict__ a, const uint8_t* __restrict__ w,
+                                           const uint8_t* cur, uint8_t* nxt, const BDmaPtrs& ptr,
+                                           bool refill, int64_t kbyte_next, int a_off, int b_off,
+                                           int h, int sw, BFrags& f0, BFrags& f1,
+                                           f32x16 (&acc)[kETM][kETN]) {
+  bdma_barrier();
+  if (refill) bdma_issue(a, w, ptr, kbyte_next, nxt);
+  bfrags<0>(cur, a_off, b_off, h, sw, f0);
+  bmfma(f1, acc);                          // previous stage, k-step 3
+  bfrags<1>(cur, a_off, b_off, h, sw, f1);
+  bmfma(f0, acc);
+  bfrags<2>(cur, a_off, b_off, h, sw, f0);
+  bmfma(f1, acc);
+  bfrags<3>(cur, a_off, b_off, h, sw, f1);
+  bmfma(f0, acc);
+#pragma unroll
+  for (int m = 0; m < kETM * kETN; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (load issue)
+  }
+#pragma unroll
+  for (int m = 0; m < 3 * kETM * kETN; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+// 32 rows x 128 columns of a wave's tile, staged in LDS, to bf16: a lane takes
+// 4 consecutive columns of a row per step, so 32 lanes cover a 128-column row
+// segment and the 8-byte stores complete whole lines.
+template <int EPI>
+__device__ __forceinline__ void bdma_slice_out(const float* st, f32x4 bv, int64_t row0, int64_t col,
+                                               int64_t M, int64_t N, bool vec,
+                                               uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63, c = lane & 31;
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int rr = it * 2 + (lane >> 5);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(st + rr * 128 + ((c ^ rr) << 2));
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v[t] = a[t] + bv[t];
+      if (EPI == 1) v[t] = gelu_erf(v[t]);
+    }
+    const u32x2 pk = {bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+    const int64_t row = row0 + rr;
+    if (vec) {
+      *reinterpret_cast<u32x2*>(y + row * N + col) = pk;
+    } else if (row < M) {
+      const uint16_t hv[4] = {(uint16_t)pk.x, (uint16_t)(pk.x >> 16), (uint16_t)pk.y, (uint16_t)(pk.y >> 16)};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (col + t < N) y[row * N + col + t] = hv[t];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kENT, 1) void gemm_bf16_dma_kernel(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const uint16_t* __restrict__ bias,
+    int64_t M, int64_t N, int64_t K, int epi, uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kEStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kEStage];
+  __shared__ __attribute__((aligned(16))) float col_bias[kEBN];
+  const int64_t tiles_m = (M + kEBM - 1) / kEBM, tiles_n = (N + kEBN - 1) / kEBN;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * kEBM, n0 = tn * kEBN;
+  {
+    const int64_t c = n0 + threadIdx.x;
+    col_bias[threadIdx.x] = (bias && c < N) ? bf16_bits_to_f32(bias[c]) : 0.0f;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, h = lane >> 5, sw = (r >> 1) & 7;
+  const int a_off = (wm * kEWM + r) * kERow, b_off = (wn * kEWN + r) * kERow;
+
+  BDmaPtrs ptr;
+  bdma_setup(M, N, K, m0, n0, ptr);
+  f32x16 acc[kETM][kETN];
+#pragma unroll
+  for (int i = 0; i < kETM; ++i)
+#pragma unroll
+    for (int j = 0; j < kETN; ++j) acc[i][j] = f32x16{};
+
+  const int ns = (int)(K / kEBK);
+  BFrags f0, f1;
+  bdma_issue(x, w, ptr, 0, lds0);
+  bdma_barrier();
+  if (ns > 1) bdma_issue(x, w, ptr, kERow, lds1);
+  bfrags<0>(lds0, a_off, b_off, h, sw, f0);
+  bfrags<1>(lds0, a_off, b_off, h, sw, f1);
+  bmfma(f0, acc);
+  bfrags<2>(lds0, a_off, b_off, h, sw, f0);
+  bmfma(f1, acc);
+  bfrags<3>(lds0, a_off, b_off, h, sw, f1);
+  bmfma(f0, acc);
+  // stage t reads buffer t % 2 and refills the other with stage t + 1; whole
+  // pairs of stages, then at most one more
+  int t = 1;
+  for (; t + 1 < ns; t += 2) {
+    bdma_stage(x, w, lds1, lds0, ptr, true, (int64_t)(t + 1) * kERow, a_off, b_off, h, sw, f0, f1,
+               acc);
+    bdma_stage(x, w, lds0, lds1, ptr, t + 2 < ns, (int64_t)(t + 2) * kERow, a_off, b_off, h, sw, f0,
+               f1, acc);
+  }
+  if (t < ns) bdma_stage(x, w, lds1, lds0, ptr, false, 0, a_off, b_off, h, sw, f0, f1, acc);
+  bmfma(f1, acc);
+
+  // epilogue: acc + bias -> GELU -> bf16, the operations of gemm_bf16_kernel
+  __syncthreads();   // every wave is done with the stage buffers
+  float* st = reinterpret_cast<float*>(lds0 + wave * 16384);
+  const bool vec = m0 + kEBM <= M && n0 + kEBN <= N && N % 4 == 0 &&
+                   (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+  const int cq = wn * kEWN + (lane & 31) * 4;             // this lane's 4 columns on read-back
+  const f32x4 bv = *reinterpret_cast<const f32x4*>(col_bias + cq);
+#pragma unroll
+  for (int i = 0; i < kETM; ++i) {
+#pragma unroll
+    for (int j = 0; j < kETN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = j * 8 + g * 2 + h;
+        *reinterpret_cast<f32x4*>(st + r * 128 + ((c ^ r) << 2)) =
+            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    const int64_t row0 = m0 + wm * kEWM + i * 32;
+    if (epi == 1)
+      bdma_slice_out<1>(st, bv, row0, n0 + cq, M, N, vec, y);
+    else
+      bdma_slice_out<0>(st, bv, row0, n0 + cq, M, N, vec, y);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // Few-row case (M <= kGemvMaxRows, e.g. the modulation linear on the timestep
 // embedding, M = 2): the weight read is the whole cost, so no tiles and no
 // MFMA.  Each wave owns kGemvRows weight rows; lane l reads 8 consecutive k
@@ -246,6 +484,23 @@ hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, int6
     case 7: return launch_gemv<7>(x, w, bias, N, K, epilogue, y, stream);
     case 8: return launch_gemv<8>(x, w, bias, N, K, epilogue, y, stream);
     default: break;
+  }
+  // the 256x256 direct-to-LDS kernel when its tiles cover at least half the
+  // compute units (measured: 0.68-0.83x the 128x128 kernel's time from 144
+  // tiles on, 1.1-1.7x at 108 and fewer) and its layout applies;
+  // NVFP4_BF16_GEMM_KERNEL=tile|dma pins one (dma only where it applies)
+  const int64_t big_tiles = ((M + kEBM - 1) / kEBM) * ((N + kEBN - 1) / kEBN);
+  const uintptr_t bits = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w);
+  const int64_t limit = (int64_t)1 << 32;
+  const bool dma_ok = K > 0 && K % kEBK == 0 && (bits & 15) == 0 && M * K * 2 < limit && N * K * 2 < limit;
+  const char* pin = getenv("NVFP4_BF16_GEMM_KERNEL");
+  const bool want_dma = pin ? strcmp(pin, "dma") == 0 : 2 * big_tiles >= compute_units();
+  if (dma_ok && want_dma) {
+    hipLaunchKernelGGL(gemm_bf16_dma_kernel, dim3((unsigned)big_tiles), dim3(kENT), 0, stream,
+                       reinterpret_cast<const uint8_t*>(x), reinterpret_cast<const uint8_t*>(w),
+                       reinterpret_cast<const uint16_t*>(bias), M, N, K, epilogue,
+                       reinterpret_cast<uint16_t*>(y));
+    return hipGetLastError();
   }
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)tiles), dim3(NT), 0, stream,

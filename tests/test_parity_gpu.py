@@ -547,6 +547,35 @@ def test_gemm_bf16_gelu(M):
     assert_gemm_close(y, ref, f"bf16 gelu M={M}")
 
 
+@pytest.mark.parametrize("kernel", ["tile", "dma"])
+@pytest.mark.parametrize("M,N,K,epi", [(300, 257, 1024, "none"), (512, 512, 64, "gelu"),
+                                       (257, 258, 128, "none"), (384, 300, 192, "gelu"),
+                                       (600, 770, 640, "none"), (513, 1024, 320, "gelu")])
+def test_gemm_bf16_kernels(monkeypatch, M, N, K, epi, kernel):
+    # both tiled kernels pinned, on shapes with one, two and an odd number of
+    # 64-wide K stages, ragged M / N tails, and full tiles with N % 4 != 0
+    monkeypatch.setenv("NVFP4_BF16_GEMM_KERNEL", kernel)
+    x = W.random_matrix(M + 7, (M, K), "normal")
+    w = W.random_matrix(N + 8, (N, K), "normal", 0.03)
+    b = W.random_matrix(K + 9, (1, N), "normal", 0.2)[0]
+    y = bits_of(nv.gemm_bf16(to_dev(x), to_dev(w), bias=to_dev(b), epilogue=epi))
+    ref = linear_bf16_fp64(x, w, b, gelu=epi == "gelu")
+    assert_gemm_close(y, ref, f"bf16 {kernel} {M}x{N}x{K} {epi}")
+
+
+@pytest.mark.parametrize("M,N,K,epi", [(4224, 9216, 3072, "gelu"), (8448, 3072, 12288, "none")])
+def test_gemm_bf16_large_sampled_rows(M, N, K, epi):
+    # sizes of a DiT block's linears at 4224 and 8448 tokens (the 256x256
+    # kernel by the default rule): sampled rows against the float64 sum
+    x = W.random_matrix(M + 11, (M, K), "normal")
+    w = W.random_matrix(N + 12, (N, K), "normal", 0.02)
+    b = W.random_matrix(N + 13, (1, N), "normal", 0.2)[0]
+    y = bits_of(nv.gemm_bf16(to_dev(x), to_dev(w), bias=to_dev(b), epilogue=epi))
+    rows = _sampled_rows(M, 40, seed=M + 1)
+    ref = linear_bf16_fp64(x[rows], w, b, gelu=epi == "gelu")
+    assert_gemm_close(y[rows], ref, f"bf16 {M}x{N}x{K}")
+
+
 def test_gemm_bf16_modulation_shape():
     # a modulation linear kept bf16: temb [2,3072] x W [18432,3072]
     temb = W.random_matrix(81, (2, 3072), "normal")
