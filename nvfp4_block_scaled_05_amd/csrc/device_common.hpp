@@ -96,6 +96,70 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return __builtin_fmaf(-az, h, __builtin_fmaxf(z, 0.0f));
 }
 
+// gelu_erf on 16 independent values, one step across all of them before the
+// next (the same operations per value, so the same bits).  One wave issues a
+// dependent chain at about half the rate of independent instructions, and
+// left to itself the compiler runs the chains one after another.  The empty
+// asm statements between the steps take all 16 values as operands, so every
+// value's step k is done before any value's step k+1; they emit nothing.
+__device__ __forceinline__ void tie16(f32x4 (&v)[4]) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+
+__device__ __forceinline__ void gelu_erf16(f32x4 (&z)[4]) {
+  f32x4 t[4], q[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[u][e] = __builtin_fmaf(__builtin_fabsf(z[u][e]), 0.353553391f, 1.0f);
+  tie16(t);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[u][e] = __builtin_amdgcn_rcpf(t[u][e]);
+  tie16(t);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[u][e] = __builtin_fmaf(0.33010265f, t[u][e], -1.0232246f);
+  tie16(q);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[u][e] = __builtin_fmaf(q[u][e], t[u][e], 0.68463063f);
+  tie16(q);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[u][e] = __builtin_fmaf(q[u][e], t[u][e], 0.36704522f);
+  tie16(q);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[u][e] = __builtin_fmaf(q[u][e], t[u][e], 1.4686911f);
+  tie16(q);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[u][e] = __builtin_fmaf(q[u][e], t[u][e], -2.827234f);
+  tie16(q);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[u][e] = __builtin_fmaf(z[u][e] * -0.72134752f, z[u][e], q[u][e]);
+  tie16(q);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[u][e] = __builtin_amdgcn_exp2f(q[u][e]);
+  tie16(q);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      z[u][e] = __builtin_fmaf(-__builtin_fabsf(z[u][e]), t[u][e] * q[u][e], __builtin_fmaxf(z[u][e], 0.0f));
+}
+
 // Running max |bf16| of two packed bf16 values (the output amax), as 16-bit
 // magnitudes: an integer max, so a NaN output makes the amax non-finite.
 __device__ __forceinline__ u16x2 amax_bf16x2(u16x2 m, uint32_t pair) {

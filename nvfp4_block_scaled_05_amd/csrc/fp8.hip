@@ -418,26 +418,34 @@ __device__ __forceinline__ void fp8_slice_out(const float* st, const float* rs, 
                                               int64_t row0, int64_t col, int64_t M, int64_t N,
                                               bool vec, uint16_t* __restrict__ y) {
   const int lane = threadIdx.x & 63, c = lane & 31;
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int rr = it * 2 + (lane >> 5);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(st + rr * 128 + ((c ^ rr) << 2));
-    const float rsc = rs[rr];
-    float v[4];
+  // four rows' reads first, then their 16 values (GELU one step across all
+  // 16), then the stores: one LDS wait per 16 values and independent chains
+  for (int it0 = 0; it0 < 16; it0 += 4) {
+    f32x4 v[4];
+    float rsc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      v[t] = __builtin_fmaf(a[t], rsc * cs[t], bv[t]);
-      if (EPI == 1) v[t] = gelu_erf(v[t]);
+    for (int u = 0; u < 4; ++u) {
+      const int rr = (it0 + u) * 2 + (lane >> 5);
+      v[u] = *reinterpret_cast<const f32x4*>(st + rr * 128 + ((c ^ rr) << 2));
+      rsc[u] = rs[rr];
     }
-    const u32x2 pk = {bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
-    const int64_t row = row0 + rr;
-    if (vec) {
-      *reinterpret_cast<u32x2*>(y + row * N + col) = pk;
-    } else if (row < M) {
-      const uint16_t hv[4] = {(uint16_t)pk.x, (uint16_t)(pk.x >> 16), (uint16_t)pk.y, (uint16_t)(pk.y >> 16)};
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (col + t < N) y[row * N + col + t] = hv[t];
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[u][t] = __builtin_fmaf(v[u][t], rsc[u] * cs[t], bv[t]);
+    if (EPI == 1) gelu_erf16(v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x2 pk = {bf16x2_rne(v[u][0], v[u][1]), bf16x2_rne(v[u][2], v[u][3])};
+      const int64_t row = row0 + (it0 + u) * 2 + (lane >> 5);
+      if (vec) {
+        *reinterpret_cast<u32x2*>(y + row * N + col) = pk;
+      } else if (row < M) {
+        const uint16_t hv[4] = {(uint16_t)pk.x, (uint16_t)(pk.x >> 16), (uint16_t)pk.y, (uint16_t)(pk.y >> 16)};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (col + t < N) y[row * N + col + t] = hv[t];
+      }
     }
   }
 }

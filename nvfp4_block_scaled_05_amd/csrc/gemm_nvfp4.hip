@@ -999,37 +999,47 @@ __device__ __forceinline__ void v5_stage(const uint8_t* __restrict__ ac, const u
 // short loop takes them back 4 consecutive columns per lane: 32 lanes cover
 // a 128-column row segment, so the 8-byte stores complete whole lines.
 template <int EPI>
-__device__ __forceinline__ float v5_finish(float a, float scale, float b) {
-  const float v = __builtin_fmaf(a, scale, b);
-  return EPI == 1 ? gelu_erf(v) : v;
-}
-
-template <int EPI>
 __device__ __forceinline__ u16x2 v5_slice_out(const float* st, float scale, f32x4 bv, int64_t row0,
                                               int64_t col, int64_t M, int64_t N, bool vec,
                                               uint16_t* __restrict__ y) {
   const int lane = threadIdx.x & 63, c = lane & 31;
   u16x2 amax = {0, 0};
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int rr = it * 2 + (lane >> 5);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(st + rr * 128 + ((c ^ rr) << 2));
-    float v[4];
+  // four rows' reads first, then their 16 values, then the stores: one LDS
+  // wait per 16 values and 16 independent chains for the scheduler to
+  // interleave (a lone dependent chain issues at about half the rate)
+  for (int it0 = 0; it0 < 16; it0 += 4) {
+    f32x4 a4[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) v[t] = v5_finish<EPI>(a[t], scale, bv[t]);
-    const u32x2 pk = {bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
-    const int64_t row = row0 + rr;
-    if (vec) {
-      *reinterpret_cast<u32x2*>(y + row * N + col) = pk;
-      amax = amax_bf16x2(amax_bf16x2(amax, pk.x), pk.y);
-    } else if (row < M) {
-      const uint16_t hv[4] = {(uint16_t)pk.x, (uint16_t)(pk.x >> 16), (uint16_t)pk.y, (uint16_t)(pk.y >> 16)};
+    for (int u = 0; u < 4; ++u) {
+      const int rr = (it0 + u) * 2 + (lane >> 5);
+      a4[u] = *reinterpret_cast<const f32x4*>(st + rr * 128 + ((c ^ rr) << 2));
+    }
+    f32x4 v[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (col + t < N) {
-          y[row * N + col + t] = hv[t];
-          amax = max_u16x2(amax, u16x2{(unsigned short)(hv[t] & 0x7FFFu), 0});
-        }
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[u][t] = __builtin_fmaf(a4[u][t], scale, bv[t]);
+    if (EPI == 1) gelu_erf16(v);
+    u32x2 pk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      pk[u] = u32x2{bf16x2_rne(v[u][0], v[u][1]), bf16x2_rne(v[u][2], v[u][3])};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t row = row0 + (it0 + u) * 2 + (lane >> 5);
+      if (vec) {
+        *reinterpret_cast<u32x2*>(y + row * N + col) = pk[u];
+        amax = amax_bf16x2(amax_bf16x2(amax, pk[u].x), pk[u].y);
+      } else if (row < M) {
+        const uint16_t hv[4] = {(uint16_t)pk[u].x, (uint16_t)(pk[u].x >> 16), (uint16_t)pk[u].y,
+                                (uint16_t)(pk[u].y >> 16)};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (col + t < N) {
+            y[row * N + col + t] = hv[t];
+            amax = max_u16x2(amax, u16x2{(unsigned short)(hv[t] & 0x7FFFu), 0});
+          }
+      }
     }
   }
   return amax;
@@ -1093,14 +1103,26 @@ __device__ __forceinline__ void v5_slice_quant(const float* st, uint16_t* st16, 
                                                bool degenerate, float s_enc, const float* e_of,
                                                const Out& out) {
   const int lane = threadIdx.x & 63, c = lane & 31;
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int rr = it * 2 + (lane >> 5);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(st + rr * 128 + ((c ^ rr) << 2));
-    float v[4];
+  // four rows' reads first, then their 16 values (as in v5_slice_out)
+  for (int it0 = 0; it0 < 16; it0 += 4) {
+    f32x4 a4[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) v[t] = v5_finish<EPI>(a[t], scale, bv[t]);
-    *reinterpret_cast<u32x2*>(st16 + rr * 136 + c * 4) = u32x2{bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+    for (int u = 0; u < 4; ++u) {
+      const int rr = (it0 + u) * 2 + (lane >> 5);
+      a4[u] = *reinterpret_cast<const f32x4*>(st + rr * 128 + ((c ^ rr) << 2));
+    }
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[u][t] = __builtin_fmaf(a4[u][t], scale, bv[t]);
+    if (EPI == 1) gelu_erf16(v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int rr = (it0 + u) * 2 + (lane >> 5);
+      *reinterpret_cast<u32x2*>(st16 + rr * 136 + c * 4) =
+          u32x2{bf16x2_rne(v[u][0], v[u][1]), bf16x2_rne(v[u][2], v[u][3])};
+    }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);                       // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();
