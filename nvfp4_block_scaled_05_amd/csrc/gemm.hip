@@ -4,9 +4,14 @@
 //
 //   Y[m,n] = bf16( epi( sum_k X[m,k]*W[n,k] + bias[n] ) ), fp32 accumulation.
 //
-// Tiling: 128x128 output tile per 256-thread workgroup, K step 64, LDS
-// double-buffered with a register prefetch of the next K step; each of the 4
-// waves owns a 64x64 sub-tile = 2x2 v_mfma_f32_32x32x16_bf16 tiles.
+// Three kernels, chosen by shape:
+//  * gemv_bf16_kernel (M <= 8): streams the weight once, no tiles;
+//  * gemm_bf16_dma_kernel (large problems): 256x256 tiles, operands loaded
+//    straight into LDS, 4 waves of 128x128;
+//  * gemm_bf16_kernel (the rest): 128x128 output tile per 256-thread
+//    workgroup, K step 64, LDS double-buffered with a register prefetch of
+//    the next K step; each of the 4 waves owns a 64x64 sub-tile = 2x2
+//    v_mfma_f32_32x32x16_bf16 tiles.
 #include <cstdlib>
 #include <cstring>
 
@@ -481,6 +486,7 @@ hipError_t launch_gemv(const void* x, const void* w, const void* bias, int64_t N
 hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, int64_t M, int64_t N,
                             int64_t K, int epilogue, void* y, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  static_assert(kGemvMaxRows == 8, "the cases below cover M = 1 .. kGemvMaxRows");
   switch (M) {   // few rows: the weight-streaming kernel
     case 1: return launch_gemv<1>(x, w, bias, N, K, epilogue, y, stream);
     case 2: return launch_gemv<2>(x, w, bias, N, K, epilogue, y, stream);

@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(
   __shared__ u32x4 stage[NW][L][128];   // wave w, slot s: 64 blocks = 128 words
   __shared__ float e_of[128];           // encode factor of every scale byte
   __shared__ uint32_t red[NW];
-  __shared__ uint32_t shared_amax, shared_ok;
+  __shared__ uint32_t shared_ok;
   const int wave = wave_id();
   const int lane = threadIdx.x & 63;
   const uint32_t lo = blockIdx.x * chunk;
