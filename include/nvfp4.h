@@ -277,11 +277,16 @@ size_t nvfp4_fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   Y[m,n] = bf16_rne( epi( sum_k X[m,k] * W[n,k] + bias[n] ) ), fp32 accumulation.
  *   x_bf16 [M, K], w_bf16 [N, K], bias_bf16 optional [N], y_bf16 [M, N];
  *   M, N >= 0, K > 0, K % 8 == 0; x / w 16-byte aligned, bias / y 2-byte aligned.
- * Kernels: M <= 8 streams the weight once (one pass, no tiles); otherwise
- * 256x256 tiles loaded straight into LDS when they cover at least half the
- * compute units, K % 64 == 0 and rows * K * 2 < 2^32 for both operands, else
- * 128x128 tiles.  The tiled kernels sum in the same order and give identical
- * bits.  NVFP4_BF16_GEMM_KERNEL=tile|dma pins one of them (dma only where it
+ * Kernels:
+ *   - M <= 8: the weight is streamed once (one pass, no tiles).
+ *   - 256x256 tiles loaded straight into LDS: when they cover at least half
+ *     the compute units, K % 64 == 0 and rows * K * 2 < 2^32 for both
+ *     operands.
+ *   - 128x128 tiles: otherwise.  When there are fewer of them than compute
+ *     units, two wave groups split K inside each tile.
+ * The 256x256 and plain 128x128 kernels sum in the same order and give
+ * identical bits; the K split adds its two halves at the end.
+ * NVFP4_BF16_GEMM_KERNEL=tile|dma|ksplit pins one of them (dma only where it
  * applies).  Returns 0, or an error code on invalid arguments or a launch
  * failure.
  */

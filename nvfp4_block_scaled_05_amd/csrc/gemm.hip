@@ -11,7 +11,9 @@
 //  * gemm_bf16_kernel (the rest): 128x128 output tile per 256-thread
 //    workgroup, K step 64, LDS double-buffered with a register prefetch of
 //    the next K step; each of the 4 waves owns a 64x64 sub-tile = 2x2
-//    v_mfma_f32_32x32x16_bf16 tiles.
+//    v_mfma_f32_32x32x16_bf16 tiles;
+//  * gemm_bf16_ksplit_kernel (fewer 128x128 tiles than compute units): the
+//    same tile with two such wave groups splitting K.
 #include <cstdlib>
 #include <cstring>
 
@@ -35,11 +37,12 @@ struct Bf16Tile {
   u32x4 v[4];
 };
 
+// tid: the thread's index within its group of NT threads
 __device__ __forceinline__ void load_bf16(const uint16_t* __restrict__ x, int64_t rows, int64_t K,
-                                          int64_t row0, int64_t k0, Bf16Tile& t) {
+                                          int64_t row0, int64_t k0, Bf16Tile& t, int tid) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int q = threadIdx.x + i * NT;
+    const int q = tid + i * NT;
     const int64_t row = row0 + (q >> 3);
     const int64_t k = k0 + (q & 7) * 8;
     if (row < rows && k < K)
@@ -49,10 +52,10 @@ __device__ __forceinline__ void load_bf16(const uint16_t* __restrict__ x, int64_
   }
 }
 
-__device__ __forceinline__ void store_bf16(const Bf16Tile& t, uint16_t* __restrict__ lds) {
+__device__ __forceinline__ void store_bf16(const Bf16Tile& t, uint16_t* __restrict__ lds, int tid) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int q = threadIdx.x + i * NT;
+    const int q = tid + i * NT;
     *reinterpret_cast<u32x4*>(lds + (q >> 3) * PITCH + (q & 7) * 8) = t.v[i];
   }
 }
@@ -61,9 +64,10 @@ __device__ __forceinline__ void store_bf16(const Bf16Tile& t, uint16_t* __restri
 
 template <bool kF16>
 __device__ __forceinline__ void mma_step(const uint16_t* __restrict__ As,
-                                         const uint16_t* __restrict__ Bs, f32x16 (&acc)[2][2]) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+                                         const uint16_t* __restrict__ Bs, f32x16 (&acc)[2][2],
+                                         int tid) {
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
   const int r = lane & 31, kh = (lane >> 5) * 8;
 #pragma unroll
@@ -144,26 +148,95 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   Bf16Tile ta, tb;
-  load_bf16(x, M, K, m0, 0, ta);
-  load_bf16(w, N, K, n0, 0, tb);
-  store_bf16(ta, lds[0][0]);
-  store_bf16(tb, lds[0][1]);
+  const int tid = threadIdx.x;
+  load_bf16(x, M, K, m0, 0, ta, tid);
+  load_bf16(w, N, K, n0, 0, tb, tid);
+  store_bf16(ta, lds[0][0], tid);
+  store_bf16(tb, lds[0][1], tid);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
     if (more) {
-      load_bf16(x, M, K, m0, (int64_t)(kt + 1) * BK, ta);
-      load_bf16(w, N, K, n0, (int64_t)(kt + 1) * BK, tb);
+      load_bf16(x, M, K, m0, (int64_t)(kt + 1) * BK, ta, tid);
+      load_bf16(w, N, K, n0, (int64_t)(kt + 1) * BK, tb, tid);
     }
-    mma_step<false>(lds[cur][0], lds[cur][1], acc);
+    mma_step<false>(lds[cur][0], lds[cur][1], acc, tid);
     if (more) {
-      store_bf16(ta, lds[cur ^ 1][0]);
-      store_bf16(tb, lds[cur ^ 1][1]);
+      store_bf16(ta, lds[cur ^ 1][0], tid);
+      store_bf16(tb, lds[cur ^ 1][1], tid);
     }
     __syncthreads();
   }
   epilogue(acc, 1.0f, bias, epi, M, N, m0, n0, y, nullptr);
+}
+
+// Few tiles (fewer 128x128 tiles than compute units): two groups of 4 waves
+// share each tile, group g taking the K steps g, g + 2, g + 4, ...; group 1
+// hands its sums to group 0 through LDS before the epilogue.  Twice the waves
+// per tile, no workspace.  (The two halves of the K sum are added at the end,
+// so the rounding differs from gemm_bf16_kernel's within fp32 accumulation.)
+__global__ __launch_bounds__(2 * NT, 1) void gemm_bf16_ksplit_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi,
+    uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][2][TILE_ELEMS];   // group, stage, operand
+  static_assert(sizeof(lds[1]) >= NT * 64 * sizeof(float), "group 1's buffers hold its sums");
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * BM;
+  const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * BN;
+  const int nk = (int)((K + BK - 1) / BK);
+  const int g = (int)(threadIdx.x / NT), tid = (int)(threadIdx.x % NT);
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  Bf16Tile ta, tb;
+  if (g < nk) {
+    load_bf16(x, M, K, m0, (int64_t)g * BK, ta, tid);
+    load_bf16(w, N, K, n0, (int64_t)g * BK, tb, tid);
+    store_bf16(ta, lds[g][0][0], tid);
+    store_bf16(tb, lds[g][0][1], tid);
+  }
+  __syncthreads();
+  const int steps = (nk + 1) / 2;          // group 0's count; group 1 has nk / 2
+  for (int s = 0; s < steps; ++s) {        // every thread reaches every barrier
+    const int cur = s & 1;
+    const int kt = g + 2 * s;
+    const bool have = kt < nk, more = kt + 2 < nk;
+    if (more) {
+      load_bf16(x, M, K, m0, (int64_t)(kt + 2) * BK, ta, tid);
+      load_bf16(w, N, K, n0, (int64_t)(kt + 2) * BK, tb, tid);
+    }
+    if (have) mma_step<false>(lds[g][cur][0], lds[g][cur][1], acc, tid);
+    if (more) {
+      store_bf16(ta, lds[g][cur ^ 1][0], tid);
+      store_bf16(tb, lds[g][cur ^ 1][1], tid);
+    }
+    __syncthreads();
+  }
+  float* red = reinterpret_cast<float*>(&lds[1][0][0][0]);   // group 1's buffers, now free
+  if (g == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((i * 2 + j) * 16 + r) * NT + tid] = acc[i][j][r];
+  }
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * NT + tid];
+    epilogue(acc, 1.0f, bias, epi, M, N, m0, n0, y, nullptr);
+  }
 }
 
 // Large problems (256x256 tiles covering at least half the compute units,
@@ -515,7 +588,17 @@ hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, int6
                        reinterpret_cast<uint16_t*>(y));
     return hipGetLastError();
   }
+  // fewer 128x128 tiles than compute units: two wave groups split K in each
+  // tile (NVFP4_BF16_GEMM_KERNEL=ksplit|tile pins one)
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const bool ksplit = pin ? strcmp(pin, "ksplit") == 0 : tiles < compute_units() && K > BK;
+  if (ksplit) {
+    hipLaunchKernelGGL(gemm_bf16_ksplit_kernel, dim3((unsigned)tiles), dim3(2 * NT), 0, stream,
+                       reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w),
+                       reinterpret_cast<const uint16_t*>(bias), M, N, K, epilogue,
+                       reinterpret_cast<uint16_t*>(y));
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)tiles), dim3(NT), 0, stream,
                      reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w),
                      reinterpret_cast<const uint16_t*>(bias), M, N, K, epilogue,

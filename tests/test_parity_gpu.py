@@ -547,17 +547,18 @@ def test_gemm_bf16_gelu(M):
     assert_gemm_close(y, ref, f"bf16 gelu M={M}")
 
 
-@pytest.mark.parametrize("kernel", ["tile", "dma"])
+@pytest.mark.parametrize("kernel", ["tile", "dma", "ksplit"])
 @pytest.mark.parametrize("M,N,K,epi", [(300, 257, 1024, "none"), (512, 512, 64, "gelu"),
                                        (257, 258, 128, "none"), (384, 300, 192, "gelu"),
                                        (600, 770, 640, "none"), (513, 1024, 320, "gelu"),
-                                       (256, 256, 32, "none"), (270, 300, 96, "gelu"),
+                                       (256, 256, 32, "none"), (270, 300, 96, "gelu"), (140, 130, 40, "gelu"),
                                        (520, 260, 160, "none"), (256, 512, 224, "none")])
 def test_gemm_bf16_kernels(monkeypatch, M, N, K, epi, kernel):
-    # both tiled kernels pinned, on shapes with one, two and an odd number of
+    # the three tiled kernels pinned, on shapes with one, two and an odd number of
     # 64-wide K stages, ragged M / N tails, full tiles with N % 4 != 0, and K
     # not a multiple of 64 (the 256x256 kernel does not apply: the pin falls
-    # back to 128x128 tiles)
+    # back to 128x128 tiles); ksplit also with a single K step (its second
+    # group then adds nothing)
     monkeypatch.setenv("NVFP4_BF16_GEMM_KERNEL", kernel)
     x = W.random_matrix(M + 7, (M, K), "normal")
     w = W.random_matrix(N + 8, (N, K), "normal", 0.03)
