@@ -90,8 +90,9 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards along tokens with no communication inside a layer; "
-              "see the design notes)", file=sys.stderr)
+              "(the path would shard along tokens, each GPU holding the full quantized "
+              "weights; inside a layer only the 4-byte amax of each dynamically quantized "
+              "tensor would be exchanged, by an all-reduce of the max)", file=sys.stderr)
         sys.exit(2)
     import torch
     import nvfp4_block_scaled_05_amd as nv

@@ -28,8 +28,8 @@ Sources (the web pages this path is built from):
 
 Where the pages are silent (element and scale encodings, rounding, bit and
 byte order, the tensor-scale formula, degenerate inputs) each function names
-the reading it implements; the readings are numbered R-1 ... R-19 and listed
-with their justification in the design notes at the repository root.
+the reading it implements; the readings are numbered R-1 ... R-19, and each
+function's docstring names the ones it follows.
 
 Module map:
   formats.py -- E2M1 element codes, E4M3 scale bytes, bf16 rounding.
