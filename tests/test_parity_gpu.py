@@ -581,6 +581,18 @@ def test_gemm_bf16_large_sampled_rows(M, N, K, epi):
     assert_gemm_close(y[rows], ref, f"bf16 {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,epi", [(16, 3072, 12288, "gelu"), (300, 2000, 6144, "none")])
+def test_gemm_bf16_few_tiles_long_k(M, N, K, epi):
+    # few 128x128 tiles and a long K: the default dispatch splits K between
+    # two wave groups in each tile; against the float64 sum, all rows
+    x = W.random_matrix(M + 21, (M, K), "normal")
+    w = W.random_matrix(N + 22, (N, K), "normal", 0.02)
+    b = W.random_matrix(N + 23, (1, N), "normal", 0.2)[0]
+    y = bits_of(nv.gemm_bf16(to_dev(x), to_dev(w), bias=to_dev(b), epilogue=epi))
+    ref = linear_bf16_fp64(x, w, b, gelu=epi == "gelu")
+    assert_gemm_close(y, ref, f"bf16 {M}x{N}x{K} {epi}")
+
+
 def test_gemm_bf16_modulation_shape():
     # a modulation linear kept bf16: temb [2,3072] x W [18432,3072]
     temb = W.random_matrix(81, (2, 3072), "normal")
