@@ -59,12 +59,16 @@ def parse():
 
 def kernel_source_hash():
     """Hash of the HIP / C++ sources the library is built from (the counter
-    summary under profiles/ is valid only for the sources it was taken on)."""
+    summary under profiles/ is valid only for the sources it was taken on).
+    The test-only probe library's sources are left out."""
+    from nvfp4_block_scaled_05_amd import build
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_block_scaled_05_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         path = os.path.join(csrc, name)
         if not os.path.isfile(path) or not name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            continue
+        if name in build.PROBE_SOURCES:
             continue
         with open(path, "rb") as f:
             h.update(name.encode() + f.read())

@@ -51,6 +51,13 @@ int nvfp4_probe_decode(const uint32_t* words, const uint32_t* sbytes, int n, uin
  * epilogue's erf-form GELU. */
 int nvfp4_probe_bf16_gelu(const float* in, int n, uint16_t* bf16, float* gelu, void* stream);
 
+/* For n binary32 inputs (n > 0, n % 16 == 0; in and out 16-byte aligned):
+ * out[i] = the GEMM epilogues' GELU taken 16 values at a time, one step
+ * across all 16 before the next (the operations of the scalar GELU above, in
+ * another order across values).  Returns 0, -1 on a null pointer, -2 on a bad
+ * n, -3 on misalignment, -7 on a launch failure. */
+int nvfp4_probe_gelu16(const float* in, int n, float* out, void* stream);
+
 /* For n bf16 patterns h = bits[i] & 0xFFFF (4-byte aligned outputs):
  *   quot[i]       = the quantizer's a / 6 of a = |h| (one multiply, two FMA
  *                   corrections);

@@ -119,6 +119,19 @@ __global__ __launch_bounds__(256) void bf16_gelu_kernel(const float* in, int n, 
   if (i + (n + 1) / 2 < n) gelu[i + (n + 1) / 2] = gelu_erf(in[i + (n + 1) / 2]);
 }
 
+// out[16 t .. 16 t + 15] = the GEMM epilogues' 16-wide GELU (gelu_erf16) of
+// in[16 t .. 16 t + 15], one thread per 16 values.
+__global__ __launch_bounds__(256) void gelu16_kernel(const float* in, int groups, float* out) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= groups) return;
+  f32x4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = reinterpret_cast<const f32x4*>(in)[4 * t + u];
+  gelu_erf16(v);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) reinterpret_cast<f32x4*>(out)[4 * t + u] = v[u];
+}
+
 // For bf16 pattern h = bits[i] & 0xFFFF: quot[i] = div6_bf16(|h|) (the
 // quotient behind the block scale), scale[i] = block_scale_e4m3(|h|, s_enc),
 // zero_codes[i] = encode8 of eight copies of h with encode factor 0 (the
@@ -191,6 +204,16 @@ int nvfp4_probe_bf16_gelu(const float* in, int n, uint16_t* bf16, float* gelu, v
   const int threads = (n + 1) / 2;
   hipLaunchKernelGGL(bf16_gelu_kernel, dim3((threads + 255) / 256), dim3(256), 0,
                      static_cast<hipStream_t>(stream), in, n, reinterpret_cast<uint32_t*>(bf16), gelu);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int nvfp4_probe_gelu16(const float* in, int n, float* out, void* stream) {
+  if (bad_ptr(in) || bad_ptr(out)) return -1;
+  if (n <= 0 || (n % 16)) return -2;
+  if ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) return -3;
+  const int groups = n / 16;
+  hipLaunchKernelGGL(gelu16_kernel, dim3((groups + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), in, groups, out);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -1,5 +1,6 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/nvfp4.h declares, and reports argument errors synchronously before
+include/nvfp4.h declares (and the probe library every function of
+include/nvfp4_isa_probe.h), and reports argument errors synchronously before
 touching a device.  Fake device pointers are plain integers that are never
 dereferenced: every call here fails validation first (or fails the device
 check on a machine without a gfx950)."""
@@ -26,10 +27,20 @@ def lib():
     return _binding.load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_probe_library_exports_every_declared_symbol(lib):
+    # the test-only library of conversion probes (built beside the main one)
+    from nvfp4_block_scaled_05_amd import build
+    probe = ctypes.CDLL(build.PROBE_LIB)
+    names = declared_functions(os.path.join(ROOT, "include", "nvfp4_isa_probe.h"))
+    assert len(names) >= 6, names
+    for n in names:
+        assert hasattr(probe, n), n
 
 
 def test_exports_every_declared_symbol(lib):

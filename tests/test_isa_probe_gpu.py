@@ -42,6 +42,7 @@ def probe():
     lib.nvfp4_probe_encode.argtypes = [I, P, I, P, P]
     lib.nvfp4_probe_decode.argtypes = [P, P, I, P, P, P, P, P]
     lib.nvfp4_probe_bf16_gelu.argtypes = [P, I, P, P, P]
+    lib.nvfp4_probe_gelu16.argtypes = [P, I, P, P]
     lib.nvfp4_probe_block_scale.argtypes = [P, I, ctypes.c_float, P, P, P, P]
     return lib
 
@@ -235,6 +236,28 @@ def test_gelu_matches_oracle(probe):
     assert rel[near & big].max() < 2e-5, rel[near & big].max()
     assert rel[big].max() < 5e-5, rel[big].max()
     assert np.all(np.abs(g[~big]) <= 1e-30)
+
+
+def test_gelu16_equals_scalar_gelu_bitwise(probe):
+    # the epilogues' 16-wide GELU against the scalar one, bit for bit, on
+    # signed zeros, subnormals, infinities, NaN, huge values and a wide sweep
+    import torch
+    special = np.array([0.0, -0.0, 1e-45, -1e-45, 1e-39, -1e-39, np.inf, -np.inf, np.nan,
+                        3.4e38, -3.4e38, 1e30, -1e30, 0.5, -0.5, -0.75, 6.0, -6.0], np.float32)
+    rng = np.random.default_rng(9)
+    z = np.concatenate([special, np.linspace(-40, 40, 200014, dtype=np.float32),
+                        (rng.standard_normal(100000) * 5).astype(np.float32),
+                        rng.integers(0, 1 << 32, 100000, dtype=np.uint64).astype(np.uint32).view(np.float32)])
+    z = z[: len(z) // 16 * 16]
+    _, g1 = _bf16_gelu(probe, z)
+    t = torch.from_numpy(np.ascontiguousarray(z)).cuda()
+    o = torch.empty_like(t)
+    assert probe.nvfp4_probe_gelu16(t.data_ptr(), len(z), o.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    g16 = o.cpu().numpy()
+    nan1, nan16 = np.isnan(g1), np.isnan(g16)
+    assert np.array_equal(nan1, nan16)
+    assert np.array_equal(g1[~nan1].view(np.uint32), g16[~nan16].view(np.uint32))
 
 
 @pytest.mark.parametrize("s_enc", [1.0, 2688.0 / 3.0, 2688.0 / 0.0123, 2688.0 / 6e4, 2688.0 / 3e-30, 1e30])
