@@ -294,3 +294,46 @@ def test_quantization_error_bounded():
     step = np.where(np.abs(val) < 2, 0.5, np.where(np.abs(val) < 4, 1.0, 2.0))
     ok = (err <= 0.5 * step * S * (1 + 1e-5)) | ((nib & 7) == 7)
     assert np.all(ok)
+
+
+# --- literal bytes: the packing order (R-10) and the scale bytes, written out
+# by hand from the definitions, so a consistent swap of the nibble order in
+# the packer and in unpack_codes fails here.  amax = 2688 = 6 * 448 makes
+# s_enc = s_dec = 1:
+#   block 0: [2688, 0 x 15]          a_b = 2688, t = 448 -> S = 0x7E (448),
+#            e = 1/448, 2688 * e = 6 -> code 7; zeros -> code 0.
+#   block 1: [6, .5, 1, 1.5, 2, 3, 4, 0, -6, -.5, -1, -1.5, -2, -3, -4, -0]
+#            a_b = 6, t = 1 -> S = 0x38 (1.0: exponent field 7, mantissa 0),
+#            e = 1; the elements are the E2M1 magnitudes themselves: codes
+#            7 1 2 3 4 5 6 0 | 15 9 10 11 12 13 14 8 (sign in bit 3).
+#   block 2: [3, 1.5, 0 x 14]        a_b = 3, t = 0.5 -> S = 0x30 (0.5:
+#            exponent field 6), e = 2: 3 -> 6 (code 7), 1.5 -> 3 (code 5).
+# Element 2j goes to the low nibble of byte j.
+_LITERAL_X = np.array([[2688.0] + [0.0] * 15
+                       + [6, .5, 1, 1.5, 2, 3, 4, 0, -6, -.5, -1, -1.5, -2, -3, -4, -0.0]
+                       + [3.0, 1.5] + [0.0] * 14], np.float32)
+_LITERAL_CODES = [0x07, 0x00, 0x00, 0x00, 0x00, 0x00, 0x00, 0x00,
+                  0x17, 0x32, 0x54, 0x06, 0x9F, 0xBA, 0xDC, 0x8E,
+                  0x57, 0x00, 0x00, 0x00, 0x00, 0x00, 0x00, 0x00]
+_LITERAL_SCALES = [0x7E, 0x38, 0x30]
+
+
+def test_literal_packed_bytes():
+    q = quantize(_bits(_LITERAL_X))
+    assert q.tensor_scale == np.float32(1.0) and not q.degenerate
+    assert q.codes.tolist() == [_LITERAL_CODES]
+    assert q.scales.tolist() == [_LITERAL_SCALES]
+
+
+def test_literal_bytes_decode():
+    # the other direction, from the same hand-written bytes: unpack_codes puts
+    # the low nibble first, and dequantize gives back the block-1 and block-2
+    # values exactly
+    codes = np.array([_LITERAL_CODES], np.uint8)
+    assert unpack_codes(codes, 48)[0, 16:20].tolist() == [7, 1, 2, 3]
+    assert unpack_codes(codes, 48)[0, 32:34].tolist() == [7, 5]
+    y = bf16_bits_to_f32(dequantize(codes, np.array([_LITERAL_SCALES], np.uint8), np.float32(1.0), 48))
+    assert y[0, 16:32].tolist() == _LITERAL_X[0, 16:32].tolist()
+    assert np.signbit(y[0, 31])                      # code 8 decodes to -0.0
+    assert y[0, 32:34].tolist() == [3.0, 1.5]
+    assert y[0, 0] == 2688.0
