@@ -1,0 +1,100 @@
+"""The Python binding rejects tensors the C ABI cannot check -- host memory,
+wrong dtypes, non-contiguous views, wrong shapes -- with ValueError before any
+pointer reaches the library.  CPU only: every case fails a check first, so no
+GPU call is made (a host pointer handed to a kernel would fault the GPU)."""
+
+import pytest
+import torch
+
+import nvfp4_block_scaled_05_amd as nv
+
+
+def bf16(*shape):
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def u8(*shape):
+    return torch.zeros(shape, dtype=torch.uint8)
+
+
+def f32(*shape):
+    return torch.zeros(shape, dtype=torch.float32)
+
+
+def nvt(rows, cols):
+    return nv.Nvfp4Tensor(u8(rows, cols // 2), u8(rows, cols // 16), f32(1), cols)
+
+
+def raises(match, fn, *args, **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(*args, **kw)
+
+
+def test_quantize_rejects_bad_inputs():
+    raises("GPU tensor", nv.quantize, bf16(4, 32))                      # host memory
+    raises("dtype", nv.quantize, torch.zeros(4, 32))                    # fp32 input
+    raises("contiguous", nv.quantize, bf16(32, 4).t())                  # transposed view
+    raises("contiguous", nv.quantize, bf16(4, 64)[:, :32])              # column slice
+    raises("2-D", nv.quantize, bf16(2, 4, 32))
+    raises("multiple of 16", nv.quantize, bf16(4, 24))
+    raises("shape", nv.quantize, bf16(4, 32), out=(u8(4, 15), u8(4, 2), f32(1)))
+    raises("tuple of 3", nv.quantize, bf16(4, 32), out=(u8(4, 16), u8(4, 2)))
+
+
+def test_quantize_checks_optional_tensors():
+    # a bad optional tensor is found before the (host) input is
+    x = bf16(4, 32)
+    raises("amax: dtype", nv.quantize, x, amax=torch.zeros(1, dtype=torch.float64))
+    raises("workspace: dtype", nv.quantize, x, workspace=f32(1024))
+    raises("dev_status: dtype", nv.quantize, x, dev_status=f32(1))
+    raises("amax: needs", nv.quantize, x, amax=f32(0))
+
+
+def test_dequantize_rejects_bad_inputs():
+    raises("Nvfp4Tensor", nv.dequantize, (u8(4, 16), u8(4, 2), f32(1), 32))
+    bad = nv.Nvfp4Tensor(u8(4, 15), u8(4, 2), f32(1), 32)
+    raises("codes: shape", nv.dequantize, bad)
+    bad = nv.Nvfp4Tensor(u8(4, 16), u8(4, 3), f32(1), 32)
+    raises("scales: shape", nv.dequantize, bad)
+    raises("GPU tensor", nv.dequantize, nvt(4, 32))
+    raises("multiple of 16", nv.dequantize, nv.Nvfp4Tensor(u8(4, 4), u8(4, 1), f32(1), 8))
+
+
+def test_gemm_rejects_bad_inputs():
+    a, w = nvt(8, 64), nvt(16, 64)
+    raises("K mismatch", nv.gemm, a, nvt(16, 32))
+    raises("epilogue", nv.gemm, a, w, epilogue="relu")
+    raises("bias: shape", nv.gemm, a, w, bias=bf16(15))
+    raises("out: dtype", nv.gemm, a, w, out=f32(8, 16))
+    raises("out: shape", nv.gemm, a, w, out=bf16(16, 8))
+    raises("y_amax: dtype", nv.gemm, a, w, y_amax=torch.zeros(1, dtype=torch.float16))
+    raises("GPU tensor", nv.gemm, a, w)
+    t = nv.Nvfp4Tensor(u8(32, 8).t(), u8(8, 4), f32(1), 64)     # transposed codes
+    raises("contiguous", nv.gemm, t, w)
+
+
+def test_gemm_quantized_rejects_bad_inputs():
+    a, w = nvt(8, 64), nvt(20, 64)
+    raises("N % 16", nv.gemm_quantized, a, w, f32(1))
+    w = nvt(32, 64)
+    raises("amax: dtype", nv.gemm_quantized, a, w, bf16(1))
+    raises("out codes: shape", nv.gemm_quantized, a, w, f32(1), out=(u8(8, 8), u8(8, 2), f32(1)))
+
+
+def test_fp8_rejects_bad_inputs():
+    raises("GPU tensor", nv.fp8_quantize, bf16(4, 32))
+    raises("contiguous", nv.fp8_quantize, bf16(32, 4).t())
+    raises("out scales: dtype", nv.fp8_quantize, bf16(4, 32), out=(u8(4, 32), bf16(4)))
+    a = nv.Fp8Tensor(u8(8, 64), f32(8))
+    raises("K mismatch", nv.fp8_gemm, a, nv.Fp8Tensor(u8(4, 32), f32(4)))
+    raises("w.scales: shape", nv.fp8_gemm, a, nv.Fp8Tensor(u8(4, 64), f32(5)))
+    raises("Fp8Tensor", nv.fp8_gemm, a, (u8(4, 64), f32(4)))
+    raises("GPU tensor", nv.fp8_gemm, a, nv.Fp8Tensor(u8(4, 64), f32(4)))
+
+
+def test_gemm_bf16_rejects_bad_inputs():
+    raises("x: dtype", nv.gemm_bf16, f32(4, 64), bf16(8, 64))
+    raises("K mismatch", nv.gemm_bf16, bf16(4, 64), bf16(8, 32))
+    raises("contiguous", nv.gemm_bf16, bf16(4, 64), bf16(64, 8).t())
+    raises("bias: shape", nv.gemm_bf16, bf16(4, 64), bf16(8, 64), bias=bf16(4))
+    raises("GPU tensor", nv.gemm_bf16, bf16(4, 64), bf16(8, 64))
