@@ -18,8 +18,18 @@ quantize / dequantize rates on the [16896,3072] activation read cold from
 HBM (rotating copies), the bf16 passthrough on a modulation-shaped layer, and the CPU
 oracle timed on a row sample of the same step.
 
+The roofline object also carries what this part sustains, measured in the
+same run by calibration kernels with known work (an fp16 MFMA loop on
+data-bearing operands, with the shader clock it ran at; streaming HBM read
+and copy), and the dominant kernel's average duration from the committed
+rocprofv3 kernel trace of this command when that trace was taken on the
+current kernel sources.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --calib-copy     (plain 1 GiB device copy, for counter calibration)
+       python bench.py --calib-copy     (1 GiB streaming copy kernel, for counter calibration)
+       python bench.py --summarize-trace kernel_trace.csv [--trace-json out.json]
+                                         (per-kernel, per-grid durations of a rocprofv3
+                                          --kernel-trace CSV; no GPU needed)
 """
 
 import argparse
@@ -52,8 +62,15 @@ def parse():
     p.add_argument("--no-graphs", action="store_true", help="skip the HIP-graph section")
     p.add_argument("--no-extras", action="store_true",
                    help="only the headline step, quantize and bf16 sections (profiling runs)")
-    p.add_argument("--cpu-rows", type=int, default=12288)
+    p.add_argument("--cpu-rows", type=int, default=2048,
+                   help="token rows of the CPU oracle's pass through the whole step")
+    p.add_argument("--cpu-g2-rows", type=int, default=64,
+                   help="rows of the exact int64 GEMM form timed per shape (extrapolated)")
     p.add_argument("--calib-copy", action="store_true")
+    p.add_argument("--summarize-trace", metavar="CSV",
+                   help="summarize a rocprofv3 kernel_trace.csv and exit")
+    p.add_argument("--trace-json", metavar="JSON", help="with --summarize-trace: also write JSON")
+    p.add_argument("--trace-command", default="", help="with --trace-json: the profiled command")
     return p.parse_args()
 
 
@@ -90,8 +107,150 @@ def measured_traffic(kernel, launches_per_step):
     return None if k is None else k.get("bytes_per_launch")
 
 
+UP_TILES = ((TOKENS + 255) // 256) * ((MLP + 255) // 256)   # 256x256 tiles of the up GEMM
+
+
+def _short_kernel_name(name):
+    """A kernel's name without namespaces and argument list, template
+    arguments kept: 'nvfp4::(anonymous namespace)::k<2>(int, ...)' -> 'k<2>'."""
+    name = name.replace("(anonymous namespace)", "anon")
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    base, depth, last = name[:cut], 0, 0
+    for i, ch in enumerate(base):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == ":" and depth == 0:
+            last = i + 1
+    return base[last:].strip()
+
+
+def summarize_trace(csv_path):
+    """Per (kernel, grid size) dispatch statistics of a rocprofv3
+    --kernel-trace CSV: launches, mean / median / min / max duration in us."""
+    import csv
+    groups = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = _short_kernel_name(row.get("Kernel_Name", ""))
+            grid = row.get("Grid_Size_X") or row.get("Grid_Size") or "0"
+            wg = row.get("Workgroup_Size_X") or row.get("Workgroup_Size") or "1"
+            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            key = (name, int(grid) // max(int(wg), 1))
+            groups.setdefault(key, []).append(dur)
+    out = []
+    for (name, wgs), d in groups.items():
+        a = np.array(d)
+        out.append({"kernel": name, "workgroups": wgs, "launches": len(d),
+                    "avg_us": round(float(a.mean()), 2), "median_us": round(float(np.median(a)), 2),
+                    "min_us": round(float(a.min()), 2), "max_us": round(float(a.max()), 2),
+                    "total_us": round(float(a.sum()), 1)})
+    out.sort(key=lambda r: -r["total_us"])
+    return out
+
+
+def print_trace_summary(rows, source_hash, command, json_path=None):
+    print("| kernel | workgroups | launches | average us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['kernel']} | {r['workgroups']} | {r['launches']} | {r['avg_us']} | "
+              f"{r['median_us']} | {r['min_us']} | {r['max_us']} |")
+    if json_path:
+        with open(json_path, "w") as f:
+            json.dump({"source_hash": source_hash, "command": command, "dispatches": rows}, f,
+                      indent=1)
+            f.write("\n")
+
+
+def profiled_up_gemm():
+    """The up GEMM's average duration in the committed kernel trace of the
+    bench command, if that trace was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "dit_mlp_2048_kernel_trace.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    for r in rec.get("dispatches", []):
+        if r["kernel"].startswith("gemm_nvfp4_v5_kernel<false>") and r["workgroups"] == UP_TILES:
+            return {"avg_launch_us": r["avg_us"], "median_us": r["median_us"],
+                    "launches": r["launches"], "command": rec.get("command", "")}
+    return None
+
+
+def calibration(ev, stream):
+    """What this part sustains, from kernels with known work (calib.h in the
+    package sources): the fp16 MFMA rate with constant and with data-bearing
+    operands and the shader clock under that load, and streaming HBM read
+    and copy rates over 1 GiB buffers (four times the last-level cache)."""
+    import ctypes
+    import torch
+    from nvfp4_block_scaled_05_amd import build
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    P = ctypes.c_void_p
+    lib.nvfp4_calib_mfma_f16.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P]
+    lib.nvfp4_calib_read.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.nvfp4_calib_copy.argtypes = [P, P, ctypes.c_size_t, P]
+    units = lib.nvfp4_calib_units()
+    sink = torch.empty(units * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(units * 4 * 2, dtype=torch.int64, device="cuda")
+    s = stream.cuda_stream
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = ev(), ev()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return float(np.median(ts))
+
+    out = {"what": "calibration kernels with known work, same run"}
+    iters = 20000
+    flop = units * 4 * iters * 16 * 32768
+    for mode, name in ((0, "mfma_f16_constant_operands"), (1, "mfma_f16_data_operands")):
+        def run(mode=mode):
+            rc = lib.nvfp4_calib_mfma_f16(iters, mode, sink.data_ptr(), clocks.data_ptr(), s)
+            if rc != 0:
+                raise RuntimeError(f"nvfp4_calib_mfma_f16: {rc}")
+        t = timed(run, 3)
+        c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+        ghz = float(np.mean(c[:, 0] / np.maximum(c[:, 1], 1))) * 0.1
+        out[name] = {"TFLOPs": round(flop / t / 1e12, 1), "clock_GHz": round(ghz, 3),
+                     "us": round(t * 1e6, 1)}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    red = torch.empty(4096, dtype=torch.int32, device="cuda")
+    t_read = timed(lambda: lib.nvfp4_calib_read(src.data_ptr(), n, red.data_ptr(), s), 5)
+    t_copy = timed(lambda: lib.nvfp4_calib_copy(src.data_ptr(), dst.data_ptr(), n, s), 5)
+    out["hbm_read_GBps"] = round(n / t_read / 1e9, 1)
+    out["hbm_copy_GBps"] = round(2 * n / t_copy / 1e9, 1)
+    del src, dst
+    return out
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        print_trace_summary(summarize_trace(args.summarize_trace), kernel_source_hash(),
+                            args.trace_command, args.trace_json)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path would shard along tokens, each GPU holding the full quantized "
@@ -103,13 +262,19 @@ def main():
     from nvfp4_block_scaled_05_amd import inputs
 
     if args.calib_copy:
+        import ctypes
+        from nvfp4_block_scaled_05_amd import build
+        lib = ctypes.CDLL(build.PROBE_LIB)
+        lib.nvfp4_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p]
         n = 1 << 30
-        a = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         b = torch.empty_like(a)
         for _ in range(5):
-            b.copy_(a)
+            lib.nvfp4_calib_copy(a.data_ptr(), b.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
-        print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n}))
+        print(json.dumps({"calib_copy_kernel": "calib_copy_kernel", "launches": 5,
+                          "bytes_read_per_launch": n, "bytes_written_per_launch": n}))
         return
 
     nv.load()
@@ -198,21 +363,34 @@ def main():
     value = 2 * GEMM_FLOP / (ms_per_step * 1e-3) / 1e12
 
     extras = SimpleNamespace(x=x, xq=xq, xq_out=xq_out, wq_up=wq_up, wq_down=wq_down, amax=amax,
-                             y=y, ws_down=ws_down, w_up=w_up, w_down=w_down, stream=stream, ev=ev,
-                             steps=args.steps, warmup=args.warmup)
+                             y=y, h=h, ws_up=ws_up, ws_down=ws_down, w_up=w_up, w_down=w_down,
+                             stream=stream, ev=ev, steps=args.steps, warmup=args.warmup)
     static = None if args.no_extras else static_section(extras)
     fp8 = None if args.no_extras else fp8_section(extras)
     yardstick = None if args.no_extras else yardstick_section(extras)
 
-    # roofline of the dominant kernel: the up GEMM
+    # roofline of the dominant kernel: the up GEMM, timed by the step's events
+    # around its call (which also enqueues the one-word zeroing of the amax
+    # the epilogue reduces into, so the figure is a little above the kernel's
+    # own duration in the kernel trace)
+    calib = calibration(ev, stream)
     up_us = stage_us["gemm_up_gelu_amax"]
     achieved = GEMM_FLOP / (up_us * 1e-6) / 1e12
     traffic = measured_traffic("gemm_nvfp4_v5_kernel", 2)
+    measured_peak = calib["mfma_f16_data_operands"]["TFLOPs"]
+    prof = profiled_up_gemm()
     roofline = {"kernel": "gemm_nvfp4_v5_kernel 256x256, 4 waves (up projection, GELU + amax epilogue)",
                 "bound": "mfma",
                 "achieved": round(achieved, 1), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_MFMA_F16, 4), "traffic": traffic,
-                "algorithmic_flop_per_launch": GEMM_FLOP, "avg_launch_us": round(up_us, 2)}
+                "algorithmic_flop_per_launch": GEMM_FLOP, "avg_launch_us": round(up_us, 2),
+                "peak_measured": measured_peak,
+                "peak_measured_what": "fp16 32x32x16 MFMA loop, data-bearing operands, same run",
+                "frac_measured": round(achieved / measured_peak, 4),
+                "clock_GHz": calib["mfma_f16_data_operands"]["clock_GHz"],
+                "profile": prof,
+                "frac_profile": (round(GEMM_FLOP / (prof["avg_launch_us"] * 1e-6) / 1e12 / PEAK_MFMA_F16, 4)
+                                 if prof else None)}
 
     # ------------------------------------- standalone quantize / dequantize --
     # R distinct copies of the activation (R * 104 MB exceeds the 256 MB
@@ -266,12 +444,14 @@ def main():
              "algorithmic_bytes": int(q_bytes),
              "quantize_us": round(q_us, 2), "quantize_GBps": round(q_bytes / q_us / 1e3, 1),
              "quantize_frac_hbm": round(q_bytes / q_us / 1e3 / PEAK_HBM, 4),
+             "quantize_frac_hbm_copy_measured": round(q_bytes / q_us / 1e3 / calib["hbm_copy_GBps"], 4),
              "quantize_kernel": "single pass (input held on chip while the amax is agreed)",
              "quantize_two_pass_us": round(q2_us, 2),
              "quantize_two_pass_GBps": round(q_bytes / q2_us / 1e3, 1),
              "quantize_amax_given_us": round(q1_us, 2),
              "quantize_amax_given_GBps": round(q_bytes / q1_us / 1e3, 1),
              "dequantize_us": round(dq_us, 2), "dequantize_GBps": round(q_bytes / dq_us / 1e3, 1),
+             "dequantize_frac_hbm": round(q_bytes / dq_us / 1e3 / PEAK_HBM, 4),
              "warm": {"method": f"one copy quantized {R} times in a row (input resident in the "
                                 "256 MB last-level cache; not an HBM figure)",
                       "quantize_us": round(qw_us, 2), "quantize_GBps": round(q_bytes / qw_us / 1e3, 1),
@@ -297,7 +477,7 @@ def main():
     # ----------------------------------------------------------- CPU oracle --
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(data, args.cpu_rows)
+        cpu = cpu_baseline(data, args.cpu_rows, args.cpu_g2_rows)
 
     rec = {
         "metric": "NVFP4 GEMM TFLOP/s + quantize HBM GB/s on DiT linear shapes (% of peak)",
@@ -315,6 +495,7 @@ def main():
         "weight_quantize_us": round(wquant_us, 2),
         "weight_quantize": "W_up [12288,3072], preallocated outputs, mean of 5 back-to-back calls",
         "roofline": roofline,
+        "calibration": calib,
         "quantize": quant,
         "bf16_passthrough": bf16_pass,
         "mfma_yardstick": yardstick,
@@ -540,22 +721,42 @@ def graph_section(to_dev, ev, stream):
                                "graph_TFLOPs": round(total / (block_graph * 1e-6) / 1e12, 1)}}
 
 
-def cpu_baseline(data, rows):
-    """The CPU oracle, untuned, on a row sample of the same step."""
+def cpu_baseline(data, rows, g2_rows):
+    """The CPU oracle as it stands (never tuned for speed), timed in the same
+    process after the GPU figures, on the same seeded inputs:
+
+      value             the MLP step's two GEMMs' FLOPs per second of the
+                        oracle's pass through the whole step (amax over all of
+                        X, quantize, float64-BLAS GEMM up + GELU, quantize H
+                        with its amax, GEMM down) on `rows` token rows, all
+                        BLAS threads;
+      quantize /        the activation [16896,3072] in full, one core (numpy's
+      dequantize        elementwise work is single-threaded), in GB/s of the
+                        same algorithmic bytes as the GPU figures;
+      gemm_fp64         the float64-BLAS form on the full single-linear, QKV
+                        and MLP shapes (operand decode, tensor scales and bf16
+                        rounding included; quantization of the inputs and the
+                        GELU not: the step above times the GELU);
+      gemm_exact_int64  the exact int64 form on `g2_rows` rows of each shape,
+                        its time per row extrapolated linearly to all rows.
+    """
     import oracle
     from oracle.formats import bf16_bits_to_f32
+    from nvfp4_block_scaled_05_amd import inputs
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count()
-    rng = np.random.default_rng(0)
-    sel = np.sort(rng.choice(TOKENS, rows, replace=False))
+    t_all = time.perf_counter()
     x = data["x"]
-    t_w = time.perf_counter()
     rwu = oracle.quantize(data["w_up"])
     rwd = oracle.quantize(data["w_down"])
-    t_w = time.perf_counter() - t_w
+
+    # the whole step on a row sample
+    rng = np.random.default_rng(0)
+    sel = np.sort(rng.choice(TOKENS, rows, replace=False))
     t0 = time.perf_counter()
     amax = np.abs(bf16_bits_to_f32(x)).max()
     rx = oracle.quantize(x[sel], amax=amax)
@@ -563,14 +764,79 @@ def cpu_baseline(data, rows):
     h_amax = np.abs(bf16_bits_to_f32(h_bits)).max()
     rh = oracle.quantize(h_bits, amax=h_amax)
     oracle.gemm_fp64(rh, rwd, MLP)
-    dt = time.perf_counter() - t0
-    flop = 2 * 2 * rows * MLP * HIDDEN
-    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+    dt_step = time.perf_counter() - t0
+    step_flop = 2 * 2 * rows * MLP * HIDDEN
+
+    # quantize / dequantize of the full activation, one core
+    act = inputs.quantize_act()["x"]
+    n_act = act.size
+    if threadpool_limits is not None:
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            qa = oracle.quantize(act)
+            t_q = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            oracle.dequantize(qa.codes, qa.scales, qa.tensor_scale, HIDDEN)
+            t_dq = time.perf_counter() - t0
+    else:
+        t0 = time.perf_counter()
+        qa = oracle.quantize(act)
+        t_q = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.dequantize(qa.codes, qa.scales, qa.tensor_scale, HIDDEN)
+        t_dq = time.perf_counter() - t0
+    qbytes = n_act * QUANT_BYTES_PER_ELEM
+    del act, qa
+
+    # float64-BLAS and exact int64 forms on the full shapes
+    small = inputs.linear_small()
+    c1 = (oracle.quantize(small["x"]), oracle.quantize(small["w"]), 1024)
+    qkv = inputs.qkv_1024()
+    c3 = (oracle.quantize(qkv["x"]), oracle.quantize(qkv["w"]), HIDDEN)
+    rx_full = oracle.quantize(x)
+    # an operand of the down projection's full shape, for timing only: the
+    # sampled rows' quantized H repeated down to 16896 rows (the float64 form
+    # does the same work whatever the codes are)
+    reps = -(-TOKENS // rows)
+    h_full = oracle.Quantized(codes=np.tile(rh.codes, (reps, 1))[:TOKENS],
+                              scales=np.tile(rh.scales, (reps, 1))[:TOKENS],
+                              tensor_scale=rh.tensor_scale, amax=rh.amax, s_enc=rh.s_enc,
+                              degenerate=rh.degenerate)
+    shapes = {"linear_128x1024x1024": (c1, False),
+              "qkv_4608x9216x3072": (c3, False),
+              "mlp_up_16896x12288x3072": ((rx_full, rwu, HIDDEN), False),
+              "mlp_down_16896x3072x12288": ((h_full, rwd, MLP), False)}
+    g3, g2 = {}, {}
+    for name, ((qa_, qw_, K), gelu) in shapes.items():
+        M, N = qa_.codes.shape[0], qw_.codes.shape[0]
+        t0 = time.perf_counter()
+        oracle.gemm_fp64(qa_, qw_, K, gelu=gelu)
+        dt = time.perf_counter() - t0
+        g3[name] = {"s": round(dt, 3), "TFLOPs": round(2 * M * N * K / dt / 1e12, 5)}
+        if M > g2_rows:
+            r = np.arange(g2_rows) * (M // g2_rows)
+            t0 = time.perf_counter()
+            oracle.gemm_exact_rows(qa_, qw_, K, r, gelu=gelu)
+            dt = time.perf_counter() - t0
+            full = dt * M / g2_rows
+            g2[name] = {"rows_timed": g2_rows, "s_timed": round(dt, 3),
+                        "s_extrapolated_all_rows": round(full, 1),
+                        "TFLOPs_extrapolated": round(2 * M * N * K / full / 1e12, 6)}
+    total = time.perf_counter() - t_all
+    return {"value": round(step_flop / dt_step / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{rows} of {TOKENS} token rows through the whole step (amax over all of X, "
-                      f"quantize, float64-BLAS GEMM up + GELU, quantize H, GEMM down); "
-                      f"weights quantized beforehand in {t_w:.1f}s (not counted)",
-            "seconds": round(dt, 2), "host": _host_info(threads)}
+            "sample": f"{rows} of {TOKENS} token rows through the whole MLP step (amax over all "
+                      f"of X, quantize, float64-BLAS GEMM up + GELU, quantize H, GEMM down); "
+                      f"weights quantized beforehand (not counted)",
+            "seconds": round(dt_step, 2),
+            "quantize_activation_16896x3072": {
+                "cores": 1, "quantize_s": round(t_q, 2), "quantize_GBps": round(qbytes / t_q / 1e9, 4),
+                "dequantize_s": round(t_dq, 2), "dequantize_GBps": round(qbytes / t_dq / 1e9, 4)},
+            "gemm_fp64_full_shapes": {"cores": int(threads), **g3},
+            "gemm_exact_int64_extrapolated": {"cores": 1, **g2},
+            "down_operand": "the sampled rows' quantized H repeated to 16896 rows (timing only)",
+            "total_cpu_seconds": round(total, 1),
+            "host": _host_info(threads)}
 
 
 def _host_info(blas_threads):

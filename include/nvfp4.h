@@ -135,10 +135,22 @@ int nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols,
                    int32_t* dev_status, void* stream);
 
 /*
- * nvfp4_dequantize -- NVFP4 back to bf16:
- *   y = bf16_rne( (value(code) * S_b) * s_dec ), binary32 products.
- * Code 8 (negative zero) gives -0.0.  Layouts as in nvfp4_quantize;
- * y_bf16 [rows, cols] must be 16-byte aligned.
+ * nvfp4_dequantize -- NVFP4 back to bf16.  [P1] "NVFP4量化" defines what a
+ * quantized element stands for under the two-level scaling: its 4-bit value
+ * times its 16-element block's scale times the FP32 per-tensor scale.  This
+ * call computes that value and rounds it to bf16:
+ *   y = bf16_rne( (value(code) * S_b) * s_dec ), binary32 products (the first
+ *   is exact; the order of the two products is this library's reading, since
+ *   the page gives no formula).
+ *
+ *   codes         [rows, cols/2] bytes, element 2j in the low nibble of byte
+ *                 j (as written by nvfp4_quantize); 8-byte aligned.
+ *   scales        [rows, cols/16] E4M3 bytes.
+ *   tensor_scale  1 device float: s_dec.
+ *   rows, cols    rows >= 0; cols > 0 and cols % 16 == 0.
+ *   y_bf16        out [rows, cols] bf16, 16-byte aligned.
+ * Code 8 (negative zero) gives -0.0.  Errors: NVFP4_ERR_NULL, _SHAPE, _ALIGN,
+ * _DEVICE, _HIP as for every call; nothing is data-dependent.
  */
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
                      const float* tensor_scale, int64_t rows, int64_t cols,

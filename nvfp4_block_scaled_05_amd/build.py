@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libnvfp4.so")
-PROBE_LIB = os.path.join(LIBDIR, "libnvfp4_isa_probe.so")
+PROBE_LIB = os.path.join(LIBDIR, "libnvfp4_probes.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -34,7 +34,9 @@ DEVICE_FLAGS = [
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-I", INCLUDE, "-Wall"]
 
 SOURCES = ["quantize.hip", "gemm_nvfp4.hip", "gemm.hip", "fp8.hip", "api.cpp"]
-PROBE_SOURCES = ["isa_probe.hip"]     # test-only library of conversion probes
+# test-only library: conversion probes and the calibration kernels of the
+# roofline measurement (isa_probe.h, calib.h beside the sources)
+PROBE_SOURCES = ["isa_probe.hip", "calib.hip"]
 
 
 def _compile(src):

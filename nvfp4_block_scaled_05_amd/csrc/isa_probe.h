@@ -1,6 +1,6 @@
 /*
- * nvfp4_isa_probe.h -- test-only probes of the gfx950 conversion helpers the
- * NVFP4 kernels use (library lib/libnvfp4_isa_probe.so).  They let a test
+ * isa_probe.h -- test-only probes of the gfx950 conversion helpers the
+ * NVFP4 kernels use (library lib/libnvfp4_probes.so).  They let a test
  * compare each helper with the CPU oracle on every input the kernels can give
  * it.  Not part of the NVFP4 computation; nothing in libnvfp4.so calls them.
  *

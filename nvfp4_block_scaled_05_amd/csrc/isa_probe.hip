@@ -1,5 +1,5 @@
 // Probes of the gfx950 conversions the NVFP4 kernels rely on, exposed through
-// include/nvfp4_isa_probe.h so tests can compare them with the CPU oracle on
+// isa_probe.h (beside this file) so tests can compare them with the CPU oracle on
 // every input the kernels can give them.  Each probe calls the same device
 // helpers the kernels call (device_common.hpp), never a copy of them.
 //
@@ -16,7 +16,7 @@
 //     corrections, the hardware E4M3 conversion, encode factor 0 for scale
 //     byte 0): every bf16 pattern.
 #include "device_common.hpp"
-#include "nvfp4_isa_probe.h"
+#include "isa_probe.h"
 
 namespace {
 

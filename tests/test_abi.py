@@ -1,6 +1,6 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/nvfp4.h declares (and the probe library every function of
-include/nvfp4_isa_probe.h), and reports argument errors synchronously before
+include/nvfp4.h declares (and the test-only probe library every function of
+its headers beside the sources), and reports argument errors synchronously before
 touching a device.  Fake device pointers are plain integers that are never
 dereferenced: every call here fails validation first (or fails the device
 check on a machine without a gfx950)."""
@@ -37,10 +37,16 @@ def test_probe_library_exports_every_declared_symbol(lib):
     # the test-only library of conversion probes (built beside the main one)
     from nvfp4_block_scaled_05_amd import build
     probe = ctypes.CDLL(build.PROBE_LIB)
-    names = declared_functions(os.path.join(ROOT, "include", "nvfp4_isa_probe.h"))
-    assert len(names) >= 6, names
-    for n in names:
+    names = declared_functions(os.path.join(build.CSRC, "isa_probe.h"))
+    calib = declared_functions(os.path.join(build.CSRC, "calib.h"))
+    assert len(names) >= 6 and len(calib) == 4, (names, calib)
+    for n in names + calib:
         assert hasattr(probe, n), n
+
+
+def test_public_include_holds_only_the_library_header():
+    # test-only headers live beside their sources, not in the public include/
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["nvfp4.h"]
 
 
 def test_exports_every_declared_symbol(lib):

@@ -1,5 +1,5 @@
 """The gfx950 conversions the kernels rely on, against the CPU oracle, on every
-input the kernels can give them (through lib/libnvfp4_isa_probe.so, which
+input the kernels can give them (through lib/libnvfp4_probes.so, which
 calls the kernels' own device helpers).
 
   * E2M1 encode: monotone in the binary32 pattern, so the exact list of
@@ -27,7 +27,7 @@ from oracle.gemm import gelu_f64
 pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PROBE_LIB = os.path.join(ROOT, "nvfp4_block_scaled_05_amd", "lib", "libnvfp4_isa_probe.so")
+PROBE_LIB = os.path.join(ROOT, "nvfp4_block_scaled_05_amd", "lib", "libnvfp4_probes.so")
 CAP = 4096
 
 
