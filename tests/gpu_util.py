@@ -41,3 +41,14 @@ def ulp_diff(y_bits, ref_bits):
     a = np.where(a & 0x8000, -(a & 0x7FFF), a)
     b = np.where(b & 0x8000, -(b & 0x7FFF), b)
     return np.abs(a - b)
+
+
+def stratified_rows(M, tile=256, block=32):
+    """Rows to compare at full size: one in every `tile`-row band of the
+    output (so every tile row of a 256x256-tiled GEMM, every band of K-split
+    tail tiles and every workgroup of the XCD-ordered grid is touched), the
+    32-row MFMA block inside the band and the row inside that block rotating
+    from band to band, plus the first and last rows."""
+    bands = -(-M // tile)
+    rows = [b * tile + block * (b % (tile // block)) + (7 * b + 3) % block for b in range(bands)]
+    return np.unique(np.clip(np.array(rows + [0, M - 1]), 0, M - 1))

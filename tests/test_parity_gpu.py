@@ -21,7 +21,7 @@ import nvfp4_block_scaled_05_amd as nv
 from nvfp4_block_scaled_05_amd import inputs as W
 from oracle import (bf16_bits_to_f32, dequantize as o_dequantize, gemm_fp64,
                     gemm_exact_rows, linear_bf16_fp64, quantize as o_quantize)
-from tests.gpu_util import bits_of, f32_dev, rel_frobenius, to_dev, ulp_diff
+from tests.gpu_util import bits_of, f32_dev, rel_frobenius, stratified_rows, to_dev, ulp_diff
 
 pytestmark = pytest.mark.gpu
 
@@ -138,7 +138,7 @@ def test_quantize_single_pass_capacity_edge(extra_rows):
     chunk = -(-nblocks // units)
     edges = [min(rows - 1, (g * chunk * 16) // 3072 + d) for g in (1, units // 2, units - 1) for d in (-1, 0)]
     rng = np.random.default_rng(extra_rows)
-    sample = np.unique(np.concatenate([[0, rows - 1], edges, rng.choice(rows, 40, replace=False)]))
+    sample = np.unique(np.concatenate([stratified_rows(rows), edges, rng.choice(rows, 40, replace=False)]))
     ref = o_quantize(bits[sample], amax=amax)
     assert np.array_equal(q.scales.cpu().numpy()[sample], ref.scales), "scales"
     assert np.array_equal(q.codes.cpu().numpy()[sample], ref.codes), "codes"
@@ -309,8 +309,10 @@ def _oracle_weight(name, seed=0):
 
 
 def _sampled_rows(M, n=96, seed=0):
+    """Rows compared at full size: one in every 256-row tile band (MFMA block
+    and row inside it rotating; stratified_rows), plus n random ones."""
     rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, n, replace=False)]))
+    return np.unique(np.concatenate([stratified_rows(M), rng.choice(M, min(n, M), replace=False)]))
 
 
 def test_gemm_qkv_1024_sampled_rows():
@@ -396,16 +398,19 @@ def test_gemm_kernels_and_k_split(monkeypatch, M, N, K, kernel, split):
     assert_gemm_close(y, ref, f"{kernel}/{split} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 520, 1152), (257, 300, 1024), (64, 33, 3072),
-                                   (513, 256, 128), (256, 256, 256), (600, 700, 384)])
-@pytest.mark.parametrize("split", [None, "3", "7"])
+_V5_SHAPES = [(300, 520, 1152), (257, 300, 1024), (64, 33, 3072), (513, 256, 128), (256, 256, 256),
+              (600, 700, 384)]
+
+
+@pytest.mark.parametrize("M,N,K,split", [(M, N, K, split) for M, N, K in _V5_SHAPES
+                                         for split in (None, "3", "7")
+                                         if split is None or int(split) <= K // 128])
 def test_gemm_v5_and_k_split(monkeypatch, M, N, K, split):
     # the direct-to-LDS kernel (K % 128 == 0) on ragged tiles, 1 to 9 stages,
     # whole and with the tail tiles' K range split over 3 or 7 workgroups
+    # (only where the K range has at least as many 128-wide stages as ways)
     monkeypatch.setenv("NVFP4_GEMM_KERNEL", "v5")
     if split:
-        if int(split) > K // 128:
-            pytest.skip("fewer stages than ways")
         monkeypatch.setenv("NVFP4_GEMM_SPLIT", split)
         assert nv.gemm_workspace(M, N, K) is not None
     for epi, bias in (("none", False), ("gelu", True)):
@@ -627,7 +632,8 @@ def test_quantize_single_pass_wait_timeout_path(shape, monkeypatch):
         return
     q = gpu_quantize(bits)
     amax = np.float32(np.abs(bf16_bits_to_f32(bits)).max())
-    rows = np.unique(np.concatenate([[0, shape[0] - 1], np.random.default_rng(3).choice(shape[0], 40, replace=False)]))
+    rows = np.unique(np.concatenate([stratified_rows(shape[0]),
+                                     np.random.default_rng(3).choice(shape[0], 40, replace=False)]))
     ref = o_quantize(bits[rows], amax=amax)
     assert np.array_equal(q.scales.cpu().numpy()[rows], ref.scales)
     assert np.array_equal(q.codes.cpu().numpy()[rows], ref.codes)
