@@ -74,6 +74,10 @@ def parse():
     return p.parse_args()
 
 
+def _progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def kernel_source_hash():
     """Hash of the HIP / C++ sources the library is built from (the counter
     summary under profiles/ is valid only for the sources it was taken on).
@@ -365,6 +369,7 @@ def main():
     extras = SimpleNamespace(x=x, xq=xq, xq_out=xq_out, wq_up=wq_up, wq_down=wq_down, amax=amax,
                              y=y, h=h, ws_up=ws_up, ws_down=ws_down, w_up=w_up, w_down=w_down,
                              stream=stream, ev=ev, steps=args.steps, warmup=args.warmup)
+    _progress(f"step timed: {ms_per_step:.3f} ms; extra sections")
     static = None if args.no_extras else static_section(extras)
     fp8 = None if args.no_extras else fp8_section(extras)
     yardstick = None if args.no_extras else yardstick_section(extras)
@@ -373,6 +378,7 @@ def main():
     # around its call (which also enqueues the one-word zeroing of the amax
     # the epilogue reduces into, so the figure is a little above the kernel's
     # own duration in the kernel trace)
+    _progress("extra sections done; calibration kernels")
     calib = calibration(ev, stream)
     up_us = stage_us["gemm_up_gelu_amax"]
     achieved = GEMM_FLOP / (up_us * 1e-6) / 1e12
@@ -471,12 +477,15 @@ def main():
                  "us": round(mod_us, 2),
                  "GBps_weight_read": round(6 * HIDDEN * HIDDEN * 2 / mod_us / 1e3, 1)}
 
+    _progress("quantize and bf16 sections done; graphs and shapes")
     graphs = None if args.no_graphs or args.no_extras else graph_section(to_dev, ev, stream)
     shapes = None if args.no_extras else shapes_section(to_dev, ev, stream)
 
     # ----------------------------------------------------------- CPU oracle --
     cpu = None
+    _progress("GPU sections done")
     if not args.no_cpu:
+        _progress("CPU oracle baseline (about a minute)")
         cpu = cpu_baseline(data, args.cpu_rows, args.cpu_g2_rows)
 
     rec = {
