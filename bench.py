@@ -227,7 +227,8 @@ def calibration(ev, stream):
     out = {"what": "calibration kernels with known work, same run"}
     iters = 20000
     flop = units * 4 * iters * 16 * 32768
-    for mode, name in ((0, "mfma_f16_constant_operands"), (1, "mfma_f16_data_operands")):
+    for mode, name in ((0, "mfma_f16_constant_operands"), (1, "mfma_f16_data_operands"),
+                       (2, "mfma_f16_nvfp4_valued_operands")):
         def run(mode=mode):
             rc = lib.nvfp4_calib_mfma_f16(iters, mode, sink.data_ptr(), clocks.data_ptr(), s)
             if rc != 0:
@@ -304,7 +305,7 @@ def main():
     # weight stays in the 256 MB last-level cache between them)
     wq_up = nv.quantize_weight(w_up)
     wq_down = nv.quantize_weight(w_down)
-    w_ws = torch.empty(nv.quantize_workspace_bytes(*w_up.shape), dtype=torch.uint8, device=dev)
+    w_ws = nv.quantize_workspace(dev)
     w_out = (wq_up.codes.clone(), wq_up.scales.clone(), wq_up.tensor_scale.clone())
     for _ in range(2):
         nv.quantize(w_up, workspace=w_ws, out=w_out)
@@ -319,7 +320,7 @@ def main():
     del w_out, w_ws
 
     # preallocated step buffers
-    ws = torch.empty(nv.quantize_workspace_bytes(TOKENS, HIDDEN), dtype=torch.uint8, device=dev)
+    ws = nv.quantize_workspace(dev)
     xq = nv.quantize(x, workspace=ws)
     amax = torch.empty(1, dtype=torch.float32, device=dev)
     ws_up = nv.gemm_workspace(TOKENS, MLP, HIDDEN, device=dev)      # K-split of the tail tiles
@@ -383,7 +384,7 @@ def main():
     up_us = stage_us["gemm_up_gelu_amax"]
     achieved = GEMM_FLOP / (up_us * 1e-6) / 1e12
     traffic = measured_traffic("gemm_nvfp4_v5_kernel", 2)
-    measured_peak = calib["mfma_f16_data_operands"]["TFLOPs"]
+    measured_peak = calib["mfma_f16_nvfp4_valued_operands"]["TFLOPs"]
     prof = profiled_up_gemm()
     roofline = {"kernel": "gemm_nvfp4_v5_kernel 256x256, 4 waves (up projection, GELU + amax epilogue)",
                 "bound": "mfma",
@@ -391,9 +392,10 @@ def main():
                 "frac": round(achieved / PEAK_MFMA_F16, 4), "traffic": traffic,
                 "algorithmic_flop_per_launch": GEMM_FLOP, "avg_launch_us": round(up_us, 2),
                 "peak_measured": measured_peak,
-                "peak_measured_what": "fp16 32x32x16 MFMA loop, data-bearing operands, same run",
+                "peak_measured_what": "fp16 32x32x16 MFMA loop on NVFP4-valued operands "
+                                      "(E2M1 x E4M3 products, as the GEMM feeds), same run",
                 "frac_measured": round(achieved / measured_peak, 4),
-                "clock_GHz": calib["mfma_f16_data_operands"]["clock_GHz"],
+                "clock_GHz": calib["mfma_f16_nvfp4_valued_operands"]["clock_GHz"],
                 "profile": prof,
                 "frac_profile": (round(GEMM_FLOP / (prof["avg_launch_us"] * 1e-6) / 1e12 / PEAK_MFMA_F16, 4)
                                  if prof else None)}
@@ -405,8 +407,7 @@ def main():
     R = 8
     act0 = to_dev(inputs.quantize_act()["x"])
     acts = [act0.clone() for _ in range(R)]
-    ws2 = [torch.empty(nv.quantize_workspace_bytes(TOKENS, HIDDEN), dtype=torch.uint8, device=dev)
-           for _ in range(R)]
+    ws2 = [nv.quantize_workspace(dev) for _ in range(R)]
     qas = [nv.quantize(acts[r], workspace=ws2[r]) for r in range(R)]
     qa_outs = [(q.codes, q.scales, q.tensor_scale) for q in qas]
     y_acts = [torch.empty_like(act0) for _ in range(R)]
@@ -654,7 +655,7 @@ def shapes_section(to_dev, ev, stream):
         N, K = wshape[k]
         x = to_dev(inputs.random_matrix(100 + M + N, (M, K)))
         qx = nv.quantize(x)
-        qws = torch.empty(nv.quantize_workspace_bytes(M, K), dtype=torch.uint8, device=x.device)
+        qws = nv.quantize_workspace(x.device)
         ws = nv.gemm_workspace(M, N, K, device=x.device)
         epi = "gelu" if k == "up" else "none"
         y = nv.gemm(qx, wq[k], epilogue=epi, workspace=ws)
@@ -694,8 +695,8 @@ def graph_section(to_dev, ev, stream):
     qx = nv.quantize(x)
     qw = nv.quantize(w)
     y = nv.gemm(qx, qw)
-    ws_x = torch.empty(nv.quantize_workspace_bytes(*x.shape), dtype=torch.uint8, device=x.device)
-    ws_w = torch.empty(nv.quantize_workspace_bytes(*w.shape), dtype=torch.uint8, device=x.device)
+    ws_x = nv.quantize_workspace(x.device)
+    ws_w = nv.quantize_workspace(x.device)
 
     def small():
         nv.quantize(x, workspace=ws_x, out=(qx.codes, qx.scales, qx.tensor_scale))

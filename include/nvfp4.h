@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 5
+#define NVFP4_ABI_VERSION 6
 #define NVFP4_BLOCK 16 /* elements per block scale, [P1] "NVFP4量化" */
 
 typedef enum {
@@ -80,9 +80,9 @@ int nvfp4_abi_version(void);
 const char* nvfp4_status_string(int status);
 
 /* Bytes of device workspace nvfp4_quantize needs for a [rows, cols] input when
- * it computes the tensor amax itself (amax_in == NULL): 4096 (partial maxima
- * and, for the single-pass kernel, its arrival counters and flags).  0 when
- * rows or cols is not positive. */
+ * it computes the tensor amax itself (amax_in == NULL): 8192 (the single-pass
+ * kernel's arrival counters, release words and partial slots, then the
+ * two-pass kernels' partial maxima).  0 when rows or cols is not positive. */
 size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
@@ -101,8 +101,13 @@ size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
  *                 as a producer computed it (the GEMM epilogue's y_amax);
  *                 the input is then read once.
  *   workspace     device scratch of at least nvfp4_quantize_workspace_bytes()
- *                 bytes, 4-byte aligned, needed only when amax_in == NULL;
- *                 contents on entry do not matter.
+ *                 bytes, 8-byte aligned, needed only when amax_in == NULL.
+ *                 It must be zero-filled once before its first use; every
+ *                 call leaves it valid for the next, so a workspace kept for
+ *                 reuse is never cleared again (no clearing launch per
+ *                 call).  It belongs to one device, and calls that share it
+ *                 must be ordered (one stream).  With other contents the
+ *                 results are unspecified.
  *   dev_status    optional device int32: written with NVFP4_OK, or
  *                 NVFP4_ERR_NONFINITE when the amax is Inf / NaN, in which
  *                 case *tensor_scale is set to NaN and codes / scales are

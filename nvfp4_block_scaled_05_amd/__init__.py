@@ -18,7 +18,7 @@ Nvfp4Tensor = namedtuple("Nvfp4Tensor", ["codes", "scales", "tensor_scale", "col
 Fp8Tensor = namedtuple("Fp8Tensor", ["codes", "scales"])   # E4M3 [rows, cols], float [rows]
 
 __all__ = ["Nvfp4Tensor", "Fp8Tensor", "Nvfp4Error", "load", "abi_version", "status_string",
-           "quantize_workspace_bytes", "quantize", "dequantize", "gemm", "gemm_workspace",
+           "quantize_workspace_bytes", "quantize_workspace", "quantize", "dequantize", "gemm", "gemm_workspace",
            "gemm_quantized", "gemm_bf16", "layer_is_quantized", "quantize_weight", "linear",
            "fp8_quantize", "fp8_gemm", "fp8_gemm_workspace"]
 
@@ -87,7 +87,7 @@ def _matrix(t, name, dtype):
     torch = _torch()
     if not isinstance(t, torch.Tensor) or t.dim() != 2:
         raise ValueError(f"{name}: expected a 2-D torch.Tensor")
-    _tensor(t, name, dtype)
+    _tensor(t, name, dtype, min_numel=0)          # zero rows: a no-op call
     return tuple(t.shape)
 
 
@@ -129,6 +129,27 @@ def quantize_workspace_bytes(rows, cols):
     return load().nvfp4_quantize_workspace_bytes(rows, cols)
 
 
+def quantize_workspace(device="cuda"):
+    """A quantizer workspace: zero-filled once here, as the library requires
+    before first use; calls keep it valid, so it is reused across calls on one
+    stream without clearing."""
+    torch = _torch()
+    return torch.zeros(load().nvfp4_quantize_workspace_bytes(1, 16), dtype=torch.uint8, device=device)
+
+
+_WORKSPACES = {}
+
+
+def _default_workspace(dev):
+    """The quantizer workspace of the current stream on `dev`, made once."""
+    torch = _torch()
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None:
+        ws = _WORKSPACES[key] = quantize_workspace(dev)
+    return ws
+
+
 def _out_tuple(out, n, name):
     if not isinstance(out, (tuple, list)) or len(out) != n:
         raise ValueError(f"{name}: expected a tuple of {n} tensors")
@@ -139,8 +160,9 @@ def quantize(x, amax=None, workspace=None, dev_status=None, out=None):
     """NVFP4-quantize a 2-D bf16 tensor.  Returns an ``Nvfp4Tensor``.
 
     amax: optional one-element float32 device tensor (a producer's amax); when
-    None the amax is computed by the library.  out: optional (codes, scales,
-    tensor_scale) tensors to write into.
+    None the amax is computed by the library, with ``workspace`` (from
+    ``quantize_workspace``; by default one kept per device and stream).  out:
+    optional (codes, scales, tensor_scale) tensors to write into.
     """
     torch = _torch()
     rows, cols = _matrix(x, "x", torch.bfloat16)
@@ -163,8 +185,7 @@ def quantize(x, amax=None, workspace=None, dev_status=None, out=None):
         ts = torch.empty((1,), dtype=torch.float32, device=dev)
     lib = load()
     if amax is None and workspace is None:
-        nbytes = lib.nvfp4_quantize_workspace_bytes(rows, cols)
-        workspace = torch.empty((max(nbytes, 4),), dtype=torch.uint8, device=dev)
+        workspace = _default_workspace(dev)
     ws_bytes = 0 if workspace is None else workspace.numel()
     _binding.check(lib.nvfp4_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(ts),
                                       _ptr(amax), _ptr(workspace), ws_bytes, _ptr(dev_status),

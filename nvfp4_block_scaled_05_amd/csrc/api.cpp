@@ -68,9 +68,9 @@ const char* nvfp4_status_string(int status) {
 
 size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || bad_dim(rows) || bad_dim(cols)) return 0;
-  // the two-pass kernels use one word per partial maximum, the single-pass
-  // kernel three counter words and one partial per compute unit
-  return 4u * (size_t)nvfp4::kMaxAmaxPartials;
+  // the single-pass kernel's arrival words and partial slots, then the
+  // two-pass kernels' partial maxima
+  return 4u * (size_t)nvfp4::kQuantWorkspaceWords;
 }
 
 int nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes,
@@ -83,7 +83,7 @@ int nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* code
   if (!empty && !amax_in && !workspace) return NVFP4_ERR_NULL;
   if (cols == 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
   if (!aligned(x_bf16, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4) ||
-      !aligned(amax_in, 4) || !aligned(workspace, 4) || !aligned(dev_status, 4))
+      !aligned(amax_in, 4) || !aligned(workspace, 8) || !aligned(dev_status, 4))
     return NVFP4_ERR_ALIGN;
   if (!empty && !amax_in && workspace_bytes < nvfp4_quantize_workspace_bytes(rows, cols))
     return NVFP4_ERR_WORKSPACE;

@@ -32,7 +32,11 @@ int nvfp4_calib_units(void);
  * mode 0: every MFMA multiplies the same two constant fragments;
  * mode 1: 4 A and 4 B fragments of pseudo-random fp16 values in (-1, 1), a
  *         different (A, B) pair for each accumulator (data-bearing operands,
- *         which draw more power than constant ones).
+ *         which draw more power than constant ones);
+ * mode 2: as mode 1 with values shaped like decoded NVFP4 operands: a random
+ *         signed E2M1 value times a random E4M3-like scale (at most 6
+ *         significant bits, the operands the block-scaled GEMM feeds its
+ *         MFMAs).
  *   sink    out, units * 256 floats (one sum of accumulators per lane).
  *   clocks  out, units * 4 pairs of uint64: per wave, the shader-clock
  *           counter (s_memtime) and the 100 MHz real-time counter

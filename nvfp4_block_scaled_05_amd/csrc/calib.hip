@@ -23,6 +23,18 @@ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   return x;
 }
 
+// An fp16 value shaped like a decoded NVFP4 operand: a signed E2M1 value
+// (code from bits 0-3) times an E4M3-like scale 2^(e-3) * (1 + m/8) (bits
+// 4-6 and 7-9): at most 6 significant bits, as the GEMM's decoded operands.
+__device__ __forceinline__ float nvfp4_like(uint32_t h) {
+  const uint32_t c = h & 7u;   // E2M1 magnitude code: 0, .5, 1, 1.5, 2, 3, 4, 6
+  const float mag = c < 2u ? 0.5f * (float)c
+                           : __builtin_ldexpf(1.0f + 0.5f * (float)(c & 1u), (int)(c >> 1) - 1);
+  const float v = (h & 8u) ? -mag : mag;
+  const float s = __builtin_ldexpf(1.0f + (float)((h >> 7) & 7u) * 0.125f, (int)((h >> 4) & 7u) - 3);
+  return v * s;
+}
+
 __global__ __launch_bounds__(kCalibThreads, 1) void calib_mfma_kernel(int iters, int mode,
                                                                       float* __restrict__ sink,
                                                                       uint64_t* __restrict__ clocks) {
@@ -32,8 +44,14 @@ __global__ __launch_bounds__(kCalibThreads, 1) void calib_mfma_kernel(int iters,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t h = mix32((blockIdx.x * kCalibThreads + threadIdx.x) * 64u + u * 8u + e);
-      const float va = mode ? (float)(h & 0xFFFFu) * (1.0f / 32768.0f) - 1.0f : 0.5f;
-      const float vb = mode ? (float)(h >> 16) * (1.0f / 32768.0f) - 1.0f : 0.25f;
+      float va = 0.5f, vb = 0.25f;
+      if (mode == 1) {
+        va = (float)(h & 0xFFFFu) * (1.0f / 32768.0f) - 1.0f;
+        vb = (float)(h >> 16) * (1.0f / 32768.0f) - 1.0f;
+      } else if (mode == 2) {
+        va = nvfp4_like(h);
+        vb = nvfp4_like(h >> 12);
+      }
       a[u][e] = (_Float16)va;
       b[u][e] = (_Float16)vb;
     }
@@ -123,7 +141,7 @@ int nvfp4_calib_units(void) { return units(); }
 
 int nvfp4_calib_mfma_f16(int iters, int mode, float* sink, uint64_t* clocks, void* stream) {
   if (!sink || !clocks) return -1;
-  if (iters < 1 || (mode != 0 && mode != 1)) return -2;
+  if (iters < 1 || mode < 0 || mode > 2) return -2;
   const int n = units();
   if (n <= 0) return -7;
   hipLaunchKernelGGL(calib_mfma_kernel, dim3(n), dim3(kCalibThreads), 0,

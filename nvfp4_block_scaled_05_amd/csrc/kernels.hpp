@@ -12,6 +12,15 @@ int compute_units();
 // Upper bound on the partial maxima the amax pass writes (workspace words).
 static constexpr int kMaxAmaxPartials = 1024;
 
+// Quantizer workspace, in 32-bit words: the single-pass kernel's arrival
+// counters, release words and tagged partial slots in [0, kQuantSyncWords)
+// (they must start zeroed and every call leaves them consistent), the
+// two-pass kernels' partial maxima after them (written before they are read
+// by every call).
+static constexpr int kQuantSyncWords = 1024;
+static constexpr int kQuantTwoPassWords = kMaxAmaxPartials;
+static constexpr int kQuantWorkspaceWords = kQuantSyncWords + kQuantTwoPassWords;
+
 int amax_partial_count(int64_t numel);
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes,

@@ -262,30 +262,40 @@ __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
 // launched cooperatively (that launch path costs tens of microseconds), so
 // nothing guarantees that all workgroups are resident together: another
 // stream's kernels may hold compute units.  The wait is therefore bounded in
-// time: a workgroup that has not been released after wait_ticks reads the
-// whole tensor for its amax itself (slow, but the same value), so the kernel
-// always completes and always gives the same bytes.
+// time: a workgroup that has not been released after wait_ticks folds the
+// partials already published and reads only the ranges of the workgroups
+// whose partial is missing (slower, but the same value), so the kernel always
+// completes and always gives the same bytes.
 static constexpr int kResThreads = 1024;
 static constexpr int kResR = 9;   // 16-element blocks per thread held in registers
 static constexpr int kResL = 4;   // ... and in LDS (4 * 32 B * 1024 = 128 KB)
 static constexpr uint64_t kResWaitTicks = 20000;   // 200 us of the 100 MHz real-time counter
 
-// Workspace words of the arrival: workgroups are dealt to kXcds groups
+// Workspace words of the arrival.  Workgroups are dealt to kXcds groups
 // (blockIdx % 8, which is also the XCD they run on); each group counts its
 // arrivals on its own 128-byte line, the last of a group counts the group in
-// on the top counter, and the last group raises every group's release flag,
+// on the top counter, and the last group raises every group's release word,
 // which that group's workgroups poll.  No line sees more than 32 arrivals or
-// pollers.  The counters and flags are cleared by a one-workgroup kernel
-// just before; the partials follow them.
+// pollers.  Nothing is ever cleared: the counters only grow (64-bit), every
+// call adds exactly the same count to each (one arrival per workgroup, one
+// workgroup per compute unit), so count / arrivals-per-call is the number of
+// calls made before -- the call's epoch -- and the release word of a group
+// holds the epoch + 1 of the last call released.  Each workgroup publishes
+// its partial max in its own slot tagged with (epoch + 1) mod 2^16, in the
+// same 32-bit atomic store, so a reader can tell a published partial from a
+// stale one by the slot alone; the counters and release words only say when
+// to look.  The workspace must hold zeros before its first use; calls then
+// keep it consistent (counters at whole multiples of a call's arrivals, slots
+// all tagged with the last epoch), which is what the next call relies on.
 static constexpr int kResLine = 32;                              // words per 128-byte line
-static constexpr int kResTop = 0;                                // top counter
-static constexpr int kResGroupCount = kResLine;                  // + 32 * g
-static constexpr int kResGroupFlag = kResLine * (1 + kXcds);     // + 32 * g
-static constexpr int kResPartials = kResLine * (1 + 2 * kXcds);  // + workgroup
-static constexpr int kResClearWords = kResPartials;
+static constexpr int kResTop = 0;                                // u64 top counter
+static constexpr int kResGroupCount = kResLine;                  // + 32 * g: u64 group counter
+static constexpr int kResGroupFlag = kResLine * (1 + kXcds);     // + 32 * g: u64 release epoch
+static constexpr int kResSlots = kResLine * (1 + 2 * kXcds);     // + workgroup: tag << 16 | max
+static constexpr int kResMaxUnits = kQuantSyncWords - kResSlots; // slots that fit
 
-__global__ __launch_bounds__(256) void clear_sync_kernel(uint32_t* p) {
-  for (int i = threadIdx.x; i < kResClearWords; i += 256) p[i] = 0u;
+__device__ __forceinline__ uint64_t* res_u64(uint32_t* sync, int word) {
+  return reinterpret_cast<uint64_t*>(sync + word);
 }
 
 __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(
@@ -296,12 +306,14 @@ __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(
   __shared__ u32x4 stage[NW][L][128];   // wave w, slot s: 64 blocks = 128 words
   __shared__ float e_of[128];           // encode factor of every scale byte
   __shared__ uint32_t red[NW];
-  __shared__ uint32_t shared_ok;
+  __shared__ uint32_t shared_ok, shared_tag;
+  __shared__ uint32_t missing[kResMaxUnits / 32];   // workgroups whose partial did not arrive
   const int wave = wave_id();
   const int lane = threadIdx.x & 63;
   const uint32_t lo = blockIdx.x * chunk;
   const uint32_t end = lo + chunk < nblocks ? lo + chunk : nblocks;   // may be below lo: empty
   const uint32_t last = end > lo ? end - 1 : nblocks - 1;
+  __shared__ uint64_t shared_count;
 
   // 1. loads: the LDS part first (no registers held), then the register part
 #pragma unroll
@@ -322,6 +334,11 @@ __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(
     a[k] = __builtin_nontemporal_load(x + 2 * blk);
     b[k] = __builtin_nontemporal_load(x + 2 * blk + 1);
   }
+  // the group counter before this workgroup arrives, read while the loads
+  // above are in flight (its value gives the call's epoch; see the arrival)
+  if (threadIdx.x == 0)
+    shared_count = __hip_atomic_load(res_u64(sync, kResGroupCount + kResLine * (blockIdx.x % kXcds)),
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // block maxima, two 16-bit magnitudes per word
   uint32_t bm[(R + L + 1) / 2];
 #pragma unroll
@@ -345,40 +362,40 @@ __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(
     m = m > p.y ? m : p.y;
   }
 
-  // 2. partial max of the workgroup, arrival, bounded wait
+  // 2. partial max of the workgroup: publish it, arrive, wait (bounded)
   m = wave_max_u32(m);
   if (lane == 0) red[wave] = m;
   __syncthreads();
+  const uint32_t grp = blockIdx.x % kXcds;
+  const uint32_t groups = gridDim.x < kXcds ? gridDim.x : kXcds;
+  const uint32_t in_group = (gridDim.x - grp + kXcds - 1) / kXcds;
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) r = r > red[w] ? r : red[w];
-    // Only agent-coherent atomic words cross between workgroups (partials,
-    // counters, flags), so ordering needs no cache write-back: each store is
-    // complete (vmcnt) before the next word is touched, and the compiler may
-    // not swap them (signal fences).
-    __hip_atomic_store(sync + kResPartials + blockIdx.x, r << 16, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    // this call's epoch, from the group counter read before any arrival of
+    // this workgroup (it lies in [epoch * in_group, (epoch + 1) * in_group))
+    const uint64_t epoch = shared_count / in_group;
+    __hip_atomic_store(sync + kResSlots + blockIdx.x, (((uint32_t)epoch + 1u) << 16) | r,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0070);             // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0070);             // vmcnt(0) lgkmcnt(0): slot written first
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const uint32_t grp = blockIdx.x % kXcds;
-    const uint32_t groups = gridDim.x < kXcds ? gridDim.x : kXcds;
-    const uint32_t in_group = (gridDim.x - grp + kXcds - 1) / kXcds;
-    if (__hip_atomic_fetch_add(sync + kResGroupCount + kResLine * grp, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT) == in_group - 1 &&
-        __hip_atomic_fetch_add(sync + kResTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            groups - 1) {
+    uint64_t* gcount = res_u64(sync, kResGroupCount + kResLine * grp);
+    if (__hip_atomic_fetch_add(gcount, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) %
+                in_group == in_group - 1 &&
+        __hip_atomic_fetch_add(res_u64(sync, kResTop), (uint64_t)1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) % groups == groups - 1) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       for (uint32_t q = 0; q < groups; ++q)
-        __hip_atomic_store(sync + kResGroupFlag + kResLine * q, 1u, __ATOMIC_RELAXED,
+        __hip_atomic_store(res_u64(sync, kResGroupFlag + kResLine * q), epoch + 1, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     bool ok = true;
-    while (__hip_atomic_load(sync + kResGroupFlag + kResLine * grp, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+    while (__hip_atomic_load(res_u64(sync, kResGroupFlag + kResLine * grp), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) != epoch + 1) {
       if (__builtin_amdgcn_s_memrealtime() - t0 > wait_ticks) {
         ok = false;
         break;
@@ -387,22 +404,49 @@ __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     shared_ok = ok;
+    shared_tag = ((uint32_t)epoch + 1u) & 0xFFFFu;
+  }
+  if (threadIdx.x < kResMaxUnits / 32) missing[threadIdx.x] = 0u;
+  __syncthreads();
+  // the partials, one slot per thread: a slot tagged with this call's epoch
+  // holds its workgroup's max.  Released, every slot is tagged or about to be
+  // (its store may still be on its way): poll it, within the same time limit.
+  // Not released in time, a slot not yet tagged is counted as missing.
+  uint32_t r = 0;
+  if (threadIdx.x < gridDim.x) {
+    const uint32_t tag = shared_tag;
+    uint32_t w = __hip_atomic_load(sync + kResSlots + threadIdx.x, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    if (shared_ok && (w >> 16) != tag) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while ((w >> 16) != tag && __builtin_amdgcn_s_memrealtime() - t0 <= wait_ticks) {
+        __builtin_amdgcn_s_sleep(1);
+        w = __hip_atomic_load(sync + kResSlots + threadIdx.x, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if ((w >> 16) == tag)
+      r = (w & 0xFFFFu) << 16;
+    else
+      atomicOr(&missing[threadIdx.x >> 5], 1u << (threadIdx.x & 31));
   }
   __syncthreads();
-  uint32_t r = 0;
-  if (shared_ok) {                                // the partials, one per thread
-    if (threadIdx.x < gridDim.x)
-      r = __hip_atomic_load(sync + kResPartials + threadIdx.x, __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT);
-    for (uint32_t i = threadIdx.x + T; i < gridDim.x; i += T) {
-      const uint32_t p = __hip_atomic_load(sync + kResPartials + i, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      r = r > p ? r : p;
-    }
-  } else {                                        // not all resident: read the whole tensor
+  // workgroups whose partial is missing (not resident in time): read their
+  // ranges here -- only theirs -- and fold them in
+  {
     u16x2 mm = {0, 0};
-    for (uint32_t w = threadIdx.x; w < 2 * nblocks; w += T) mm = max_u16x2(mm, max8(x[w]));
-    r = (uint32_t)(mm.x > mm.y ? mm.x : mm.y) << 16;
+    for (int i = 0; i < kResMaxUnits / 32; ++i) {
+      uint32_t bits = missing[i];                 // the same word for every thread
+      while (bits) {
+        const uint32_t g = 32u * i + (uint32_t)__builtin_ctz(bits);
+        bits &= bits - 1u;
+        const uint32_t glo = g * chunk;
+        const uint32_t gend = glo + chunk < nblocks ? glo + chunk : nblocks;
+        for (uint32_t w = 2 * glo + threadIdx.x; w < 2 * gend; w += T) mm = max_u16x2(mm, max8(x[w]));
+      }
+    }
+    const uint32_t f = (uint32_t)(mm.x > mm.y ? mm.x : mm.y) << 16;
+    r = r > f ? r : f;
   }
   r = wave_max_u32(r);
   __syncthreads();                                // red[] is free again
@@ -497,9 +541,10 @@ int amax_partial_count(int64_t numel) {
 // fits on chip (at most units * (R + L) * 1024 blocks of 16: 109 MB of bf16 on
 // 256 compute units), it is at least kResMinElems elements (below that the
 // two launches of the two-pass kernels cost no more: both are about 15 us
-// there), and the workspace holds the counters, the flags and one partial per
-// compute unit.  NVFP4_QUANT_KERNEL=twopass turns it off, =resident lifts the
-// size floor.
+// there), and the workspace holds the counters, the release words and one
+// slot per compute unit.  NVFP4_QUANT_KERNEL=twopass turns it off, =resident
+// lifts the size floor.  One launch per call: the arrival words are never
+// cleared (see above), so no clearing kernel runs before it.
 static constexpr int64_t kResMinElems = (int64_t)3 << 23;   // 25.2 M elements
 
 static bool try_resident(const u32x4* xv, int64_t nblocks, u32x2* codes, uint8_t* scales,
@@ -511,13 +556,12 @@ static bool try_resident(const u32x4* xv, int64_t nblocks, u32x2* codes, uint8_t
   if (!forced && nblocks * 16 < kResMinElems) return false;
   const int units = compute_units();
   if (nblocks > (int64_t)units * (kResR + kResL) * kResThreads) return false;
-  if (workspace_bytes < 4u * (size_t)(kResPartials + units)) return false;
-  hipLaunchKernelGGL(clear_sync_kernel, dim3(1), dim3(256), 0, stream, workspace);
-  if (hipGetLastError() != hipSuccess) return false;
+  if (units > kResMaxUnits || workspace_bytes < 4u * (size_t)kQuantSyncWords) return false;
   uint32_t nb = (uint32_t)nblocks;
   uint32_t chunk = (uint32_t)((nblocks + units - 1) / units);
-  // NVFP4_QUANT_WAIT_TICKS shortens the wait (tests: 0 sends most
-  // workgroups down the read-everything path)
+  // NVFP4_QUANT_WAIT_TICKS shortens the wait (tests: 0 sends the
+  // workgroups not released at once down the path that reads the missing
+  // partials' ranges themselves)
   uint64_t wait_ticks = kResWaitTicks;
   if (const char* w = getenv("NVFP4_QUANT_WAIT_TICKS")) wait_ticks = strtoull(w, nullptr, 10);
   hipLaunchKernelGGL(quantize_resident_kernel, dim3(units), dim3(kResThreads), 0, stream, xv, nb,
@@ -556,15 +600,16 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* c
     if (g > qs.amax_grid) g = qs.amax_grid;
     const int64_t n16 = numel / 8;
     const int64_t chunk = (n16 + g - 1) / g;
+    uint32_t* partials = workspace + kQuantSyncWords;   // past the single-pass words
     if (qs.amax_u == 4)
-      hipLaunchKernelGGL(amax_partial_kernel<4>, dim3(g), dim3(kQuantThreads), 0, stream, xv, n16, chunk, workspace);
+      hipLaunchKernelGGL(amax_partial_kernel<4>, dim3(g), dim3(kQuantThreads), 0, stream, xv, n16, chunk, partials);
     else if (qs.amax_u == 16)
-      hipLaunchKernelGGL(amax_partial_kernel<16>, dim3(g), dim3(kQuantThreads), 0, stream, xv, n16, chunk, workspace);
+      hipLaunchKernelGGL(amax_partial_kernel<16>, dim3(g), dim3(kQuantThreads), 0, stream, xv, n16, chunk, partials);
     else
-      hipLaunchKernelGGL(amax_partial_kernel<8>, dim3(g), dim3(kQuantThreads), 0, stream, xv, n16, chunk, workspace);
+      hipLaunchKernelGGL(amax_partial_kernel<8>, dim3(g), dim3(kQuantThreads), 0, stream, xv, n16, chunk, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    words = workspace;
+    words = partials;
     n_words = g;
   }
   const int u = qs.quant_u == 1 || qs.quant_u == 4 ? qs.quant_u : 2;

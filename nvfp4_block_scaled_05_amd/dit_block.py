@@ -14,7 +14,7 @@ projection takes its input from the caller.
 """
 
 from . import (gemm, gemm_bf16, gemm_workspace, layer_is_quantized, quantize,
-               quantize_workspace_bytes, quantize_weight)
+               quantize_workspace, quantize_weight)
 
 #: layer name -> (input, weight, epilogue)
 LAYERS = {
@@ -57,9 +57,7 @@ class DitBlockLinears:
                                    torch.empty((1,), dtype=torch.float32, device=dev))
                 self.ws[name] = gemm_workspace(rows[x], n, k, device=dev)
         self.amax = torch.empty((1,), dtype=torch.float32, device=dev)
-        qws = max(quantize_workspace_bytes(rows[x], weights[w].shape[1])
-                  for x, w, _ in LAYERS.values())
-        self.quant_ws = torch.empty((qws,), dtype=torch.uint8, device=dev)
+        self.quant_ws = quantize_workspace(dev)
         names = list(LAYERS)
         # the up projection's epilogue amax feeds the down projection's quantize
         self.chain = self.quantized[names[3]] and self.quantized[names[4]]

@@ -58,7 +58,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.nvfp4_abi_version() == 5
+    assert lib.nvfp4_abi_version() == 6
     for code in range(-8, 1):
         assert lib.nvfp4_status_string(code)
     assert lib.nvfp4_status_string(-99) == b"unknown status"
@@ -69,14 +69,14 @@ def test_workspace_bytes(lib):
     assert lib.nvfp4_quantize_workspace_bytes(-1, 16) == 0
     small = lib.nvfp4_quantize_workspace_bytes(1, 16)
     big = lib.nvfp4_quantize_workspace_bytes(16896, 3072)
-    assert 4 <= small <= big <= 4096 and big % 4 == 0
+    assert small == big == 8192
 
 
 A = 1 << 20        # fake, 16-byte aligned, never dereferenced
 S = 64
 
 
-def q(lib, x=A, rows=4, cols=32, codes=A, scales=A, ts=A, amax=None, ws=A, wsb=4096, st=None):
+def q(lib, x=A, rows=4, cols=32, codes=A, scales=A, ts=A, amax=None, ws=A, wsb=8192, st=None):
     return lib.nvfp4_quantize(x, rows, cols, codes, scales, ts, amax, ws, wsb, st, None)
 
 
@@ -90,7 +90,9 @@ def test_quantize_argument_errors(lib):
     assert q(lib, x=A + 8) == ALIGN
     assert q(lib, codes=A + 4) == ALIGN
     assert q(lib, ts=A + 2) == ALIGN
+    assert q(lib, ws=A + 4) == ALIGN                # 64-bit arrival counters
     assert q(lib, wsb=0) == WORKSPACE
+    assert q(lib, wsb=4096) == WORKSPACE
     # workspace not needed when the producer's amax is given
     assert q(lib, ws=None, wsb=0, amax=A) in (OK, DEVICE)
 

@@ -98,3 +98,10 @@ def test_gemm_bf16_rejects_bad_inputs():
     raises("contiguous", nv.gemm_bf16, bf16(4, 64), bf16(64, 8).t())
     raises("bias: shape", nv.gemm_bf16, bf16(4, 64), bf16(8, 64), bias=bf16(4))
     raises("GPU tensor", nv.gemm_bf16, bf16(4, 64), bf16(8, 64))
+
+
+def test_empty_inputs_pass_the_layout_checks():
+    # zero rows is a valid (no-op) call: only the device check stops it here
+    raises("GPU tensor", nv.quantize, bf16(0, 64))
+    raises("GPU tensor", nv.fp8_quantize, bf16(0, 64))
+    raises("GPU tensor", nv.gemm_bf16, bf16(0, 64), bf16(8, 64))

@@ -39,8 +39,8 @@ def _linear_small_fn(x, w):
     qw = (torch.empty((n, k // 2), dtype=torch.uint8, device="cuda"),
           torch.empty((n, k // 16), dtype=torch.uint8, device="cuda"),
           torch.empty((1,), dtype=torch.float32, device="cuda"))
-    ws = torch.empty((4096,), dtype=torch.uint8, device="cuda")
-    ws2 = torch.empty((4096,), dtype=torch.uint8, device="cuda")
+    ws = nv.quantize_workspace()
+    ws2 = nv.quantize_workspace()
     y = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda")
 
     def fn():
@@ -114,7 +114,7 @@ def test_dynamic_quantize_graph_replays(kernel, monkeypatch):
     monkeypatch.setenv("NVFP4_QUANT_KERNEL", kernel)
     bits = W.random_matrix(41, (300, 1024), "outliers")
     x = to_dev(bits)
-    ws = torch.empty((4096,), dtype=torch.uint8, device="cuda")
+    ws = nv.quantize_workspace()
     out = (torch.empty((300, 512), dtype=torch.uint8, device="cuda"),
            torch.empty((300, 64), dtype=torch.uint8, device="cuda"),
            torch.empty((1,), dtype=torch.float32, device="cuda"))

@@ -640,6 +640,37 @@ def test_quantize_single_pass_wait_timeout_path(shape, monkeypatch):
     assert q.tensor_scale.cpu().numpy().view(np.uint32)[0] == np.float32(ref.tensor_scale).view(np.uint32)
 
 
+def test_quantize_workspace_reused_across_kernels(monkeypatch):
+    # one zero-filled workspace for many calls: the single-pass kernel never
+    # clears its arrival words (each call leaves them ready for the next) and
+    # the two-pass kernels' partial maxima sit past them, so interleaved calls
+    # of both, on two tensors, all give the oracle's bytes
+    ws = nv.quantize_workspace()
+    cases = [(W.random_matrix(61, (300, 1024), "outliers"), None),
+             (W.random_matrix(62, (513, 1024), "t3"), None)]
+    cases = [(b, o_quantize(b), to_dev(b)) for b, _ in cases]
+    for kernel in ("resident", "twopass", "resident", "resident", "twopass", "small", "resident"):
+        monkeypatch.setenv("NVFP4_QUANT_KERNEL", kernel)
+        for bits, ref, x in cases:
+            if kernel == "small" and bits.size > (1 << 18):
+                continue
+            q = nv.quantize(x, workspace=ws)
+            _sync()
+            assert_quant_equal(q, ref, f"{kernel} {bits.shape}")
+
+
+def test_quantize_default_workspace_many_calls():
+    # the binding's own workspace (one per device and stream, zeroed once):
+    # the activation [16896,3072] quantized repeatedly, every call bit-exact
+    bits = W.quantize_act()["x"]
+    ref = o_quantize(bits)
+    x = to_dev(bits)
+    for _ in range(5):
+        q = nv.quantize(x)
+        _sync()
+        assert_quant_equal(q, ref, "repeat")
+
+
 @pytest.mark.parametrize("M,N,K", [(3, 40, 8192), (70, 300, 12288)])
 def test_gemm_long_k_small_output(M, N, K):
     # a long K sends even a small output to the 256x256 kernel, whose grid of
