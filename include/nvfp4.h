@@ -140,6 +140,28 @@ int nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols,
                    int32_t* dev_status, void* stream);
 
 /*
+ * nvfp4_quantize_no_alloc -- nvfp4_quantize with the amax computed here and
+ * no workspace argument: for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It allocates nothing: its kernels use a scratch array the
+ * library owns, 8192 bytes per GPU (the whole of what the quantizer needs
+ * for any input this ABI accepts), created zero-filled when the library's
+ * code object is loaded on that GPU and kept until the process ends.
+ *
+ *   x_bf16, rows, cols, codes, scales, tensor_scale, dev_status
+ *                 as nvfp4_quantize (same checks, same bytes).
+ * Every call on one GPU shares that GPU's scratch, and each call leaves it
+ * ready for the next, so calls on one GPU must be ordered (one stream, or
+ * explicit synchronization); calls that overlap on one GPU race.  Returns
+ * NVFP4_ERR_WORKSPACE if an input ever needed more scratch than the array
+ * holds (none does), NVFP4_ERR_HIP if the array's device address cannot be
+ * looked up (once per device, on the first call there).
+ */
+int nvfp4_quantize_no_alloc(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes,
+                            uint8_t* scales, float* tensor_scale, int32_t* dev_status,
+                            void* stream);
+
+/*
  * nvfp4_dequantize -- NVFP4 back to bf16.  [P1] "NVFP4量化" defines what a
  * quantized element stands for under the two-level scaling: its 4-bit value
  * times its 16-element block's scale times the FP32 per-tensor scale.  This

@@ -27,6 +27,7 @@ SIGNATURES = {
     "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nvfp4_quantize_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "nvfp4_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
+    "nvfp4_quantize_no_alloc": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_dequantize": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P]),
     "nvfp4_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P,
                                   _P, ctypes.c_size_t, _P]),
@@ -51,20 +52,33 @@ class Nvfp4Error(RuntimeError):
         super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}")
 
 
+class _SignedLibrary:
+    """The loaded library, exposing only the functions in SIGNATURES (each
+    with its argument and result types set).  A function called without its
+    argument types would have its pointer arguments cut to a C int by ctypes;
+    here such a call fails with AttributeError instead of reaching the GPU."""
+
+    def __init__(self, lib):
+        self._lib = lib
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+            setattr(self, name, fn)
+
+    def __getattr__(self, name):
+        raise AttributeError(f"{name}: not an exported function with a declared signature")
+
+
 def load(path=LIB_PATH):
-    """Load (once) and return the ctypes library; raises if it is not built."""
+    """Load (once) and return the library; raises if it is not built."""
     global _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(path):
                 raise RuntimeError(
                     f"{path} is not built; run `python -m nvfp4_block_scaled_05_amd.build`")
-            lib = ctypes.CDLL(path)
-            for name, (res, args) in SIGNATURES.items():
-                fn = getattr(lib, name)
-                fn.restype = res
-                fn.argtypes = args
-            _lib = lib
+            _lib = _SignedLibrary(ctypes.CDLL(path))
         return _lib
 
 

@@ -96,6 +96,29 @@ int nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* code
                                            static_cast<hipStream_t>(stream)));
 }
 
+int nvfp4_quantize_no_alloc(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes,
+                            uint8_t* scales, float* tensor_scale, int32_t* dev_status,
+                            void* stream) {
+  if (bad_dim(rows) || bad_dim(cols) || rows * cols >= ((int64_t)1 << 40)) return NVFP4_ERR_SHAPE;
+  const bool empty = rows == 0;
+  if (!tensor_scale) return NVFP4_ERR_NULL;
+  if (!empty && (!x_bf16 || !codes || !scales)) return NVFP4_ERR_NULL;
+  if (cols == 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4) ||
+      !aligned(dev_status, 4))
+    return NVFP4_ERR_ALIGN;
+  if (nvfp4_quantize_workspace_bytes(rows, cols) > nvfp4::static_scratch_bytes())
+    return NVFP4_ERR_WORKSPACE;
+  int st = check_device();
+  if (st != NVFP4_OK) return st;
+  if (empty) return NVFP4_OK;
+  uint32_t* ws = nullptr;
+  if (nvfp4::static_scratch(&ws) != hipSuccess) return NVFP4_ERR_HIP;
+  return hip_status(nvfp4::launch_quantize(x_bf16, rows, cols, codes, scales, tensor_scale,
+                                           nullptr, ws, nvfp4::static_scratch_bytes(), dev_status,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                      int64_t rows, int64_t cols, void* y_bf16, void* stream) {
   if (bad_dim(rows) || bad_dim(cols) || rows * cols >= ((int64_t)1 << 40)) return NVFP4_ERR_SHAPE;

@@ -23,6 +23,12 @@ static constexpr int kQuantWorkspaceWords = kQuantSyncWords + kQuantTwoPassWords
 
 int amax_partial_count(int64_t numel);
 
+// The library-owned quantizer workspace of the current device (a static
+// device array of static_scratch_bytes(), zero when loaded): its device
+// address, looked up once per device.
+hipError_t static_scratch(uint32_t** out);
+size_t static_scratch_bytes();
+
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, float* tensor_scale, const float* amax_in,
                            uint32_t* workspace, size_t workspace_bytes, int32_t* dev_status,

@@ -26,9 +26,11 @@
 // correctly rounded (no fast-math) and the file is built with FP contraction
 // off, so every value equals the CPU oracle's bit for bit.
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -635,6 +637,44 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
                      reinterpret_cast<const uint32_t*>(codes), scales, tensor_scale, nhalves,
                      reinterpret_cast<u32x4*>(y));
   return hipGetLastError();
+}
+
+// ---------------------------------------------------- library-owned scratch --
+// The quantizer workspace of nvfp4_quantize_no_alloc, for callers that cannot
+// allocate: one copy of this array per GPU, created zero-filled when the code
+// object is loaded on that GPU (the state the single-pass kernel's arrival
+// words need before their first use; each call leaves them valid for the
+// next) and held until the process ends.  In host code the name `scratch`
+// is a host-side stand-in, not a device address: the device address comes
+// from hipGetSymbolAddress, once per device with that device current, and
+// only that address is passed to kernels.
+static __device__ __align__(256) uint32_t scratch[kQuantWorkspaceWords] = {};
+
+static constexpr int kMaxScratchDevices = 64;
+static std::atomic<uint32_t*> g_scratch[kMaxScratchDevices];
+static std::mutex g_scratch_lock;
+
+size_t static_scratch_bytes() { return sizeof(uint32_t) * kQuantWorkspaceWords; }
+
+hipError_t static_scratch(uint32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  uint32_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_lock);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      p = static_cast<uint32_t*>(addr);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 }  // namespace nvfp4

@@ -51,7 +51,7 @@ def test_public_include_holds_only_the_library_header():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
         assert n in _binding.SIGNATURES, n
@@ -95,6 +95,20 @@ def test_quantize_argument_errors(lib):
     assert q(lib, wsb=4096) == WORKSPACE
     # workspace not needed when the producer's amax is given
     assert q(lib, ws=None, wsb=0, amax=A) in (OK, DEVICE)
+
+
+def test_quantize_no_alloc_argument_errors(lib):
+    def qn(x=A, rows=4, cols=32, codes=A, scales=A, ts=A, st=None):
+        return lib.nvfp4_quantize_no_alloc(x, rows, cols, codes, scales, ts, st, None)
+    assert qn(x=None) == NULL
+    assert qn(ts=None) == NULL
+    assert qn(rows=-1) == SHAPE
+    assert qn(cols=24) == SHAPE
+    assert qn(x=A + 8) == ALIGN
+    assert qn(codes=A + 4) == ALIGN
+    assert qn(st=A + 2) == ALIGN
+    assert qn() in (OK, DEVICE)
+    assert qn(rows=0, x=None, codes=None, scales=None) in (OK, DEVICE)
 
 
 def test_quantize_valid_args_reach_device_check(lib):
