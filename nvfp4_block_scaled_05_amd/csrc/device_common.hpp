@@ -374,12 +374,12 @@ struct SplitK {
   int ways;            // K ranges per tail tile (1: no split)
 };
 
-// Work of this workgroup: tile (tm, tn), and for a tail tile its index among
-// the tail tiles and its split (split < 0 for a whole tile).
-__device__ __forceinline__ void split_coords(int64_t tiles_m, int64_t tiles_n, const SplitK& sk,
-                                             int64_t& tm, int64_t& tn, int64_t& tail,
-                                             int& split) {
-  const int64_t b = blockIdx.x;
+// Work item b: tile (tm, tn), and for a tail tile its index among the tail
+// tiles and its split (split < 0 for a whole tile).  Item b runs on XCD b % 8
+// (one item per workgroup, or a persistent grid that is a multiple of 8).
+__device__ __forceinline__ void split_coords_of(int64_t b, int64_t tiles_m, int64_t tiles_n,
+                                                const SplitK& sk, int64_t& tm, int64_t& tn,
+                                                int64_t& tail, int& split) {
   if (b < sk.main_tiles) {
     grouped_tile(xcd_order(b, sk.main_tiles), tiles_m, tiles_n, tm, tn);
     tail = -1;
@@ -390,6 +390,13 @@ __device__ __forceinline__ void split_coords(int64_t tiles_m, int64_t tiles_n, c
     split = (int)(u - tail * sk.ways);
     grouped_tile(sk.main_tiles + tail, tiles_m, tiles_n, tm, tn);
   }
+}
+
+// Work of this workgroup (one item per workgroup).
+__device__ __forceinline__ void split_coords(int64_t tiles_m, int64_t tiles_n, const SplitK& sk,
+                                             int64_t& tm, int64_t& tn, int64_t& tail,
+                                             int& split) {
+  split_coords_of(blockIdx.x, tiles_m, tiles_n, sk, tm, tn, tail, split);
 }
 
 // Tile index of this workgroup: XCD-contiguous ranges, then row-grouped order.

@@ -1045,10 +1045,10 @@ __device__ __forceinline__ u16x2 v5_slice_out(const float* st, float scale, f32x
   return amax;
 }
 
-__device__ __forceinline__ void v5_epilogue(const f32x16 (&acc)[kVTM][kVTN], float scale,
-                                            const float* col_bias, int epi, int64_t M, int64_t N,
-                                            int64_t m0, int64_t n0, uint16_t* __restrict__ y,
-                                            uint32_t* __restrict__ y_amax, float* st) {
+__device__ __forceinline__ u16x2 v5_epilogue(const f32x16 (&acc)[kVTM][kVTN], float scale,
+                                             const float* col_bias, int epi, int64_t M, int64_t N,
+                                             int64_t m0, int64_t n0, uint16_t* __restrict__ y,
+                                             float* st) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, r = lane & 31, h = lane >> 5;
   const bool vec = m0 + kVBM <= M && n0 + kVBN <= N && N % 4 == 0 &&
@@ -1077,19 +1077,7 @@ __device__ __forceinline__ void v5_epilogue(const f32x16 (&acc)[kVTM][kVTN], flo
     __builtin_amdgcn_s_waitcnt(0xC07F);                     // reads done before the next slice's writes
     __builtin_amdgcn_wave_barrier();
   }
-  if (y_amax) {   // one atomic per workgroup
-    __shared__ uint32_t wave_amax[kVNT / 64];
-    uint32_t a = (uint32_t)(amax.x > amax.y ? amax.x : amax.y) << 16;
-    a = wave_max_u32(a);
-    if (lane == 0) wave_amax[wave] = a;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t m = 0;
-#pragma unroll
-      for (int w = 0; w < kVNT / 64; ++w) m = max(m, wave_amax[w]);
-      atomicMax(y_amax, m);
-    }
-  }
+  return amax;   // this lane's max |bf16 y| (16-bit magnitudes)
 }
 
 // NVFP4 output of v5 under the static tensor scale derived from
@@ -1185,95 +1173,158 @@ __device__ __forceinline__ void v5_epilogue_quant(const f32x16 (&acc)[kVTM][kVTN
   }
 }
 
+// Work item b of a v5 launch: a whole tile, or one K range of a tail tile
+// (split_coords on item b), with its first and last stage.
+struct V5Item {
+  int64_t m0, n0, tail;
+  int split, kb, ke;
+};
+
+__device__ __forceinline__ V5Item v5_item(int64_t b, int64_t tiles_m, int64_t tiles_n,
+                                          const SplitK& sk, int nk) {
+  V5Item it;
+  int64_t tm, tn;
+  split_coords_of(b, tiles_m, tiles_n, sk, tm, tn, it.tail, it.split);
+  it.m0 = tm * kVBM;
+  it.n0 = tn * kVBN;
+  it.kb = it.split < 0 ? 0 : (int)((int64_t)it.split * nk / sk.ways);
+  it.ke = it.split < 0 ? nk : (int)((int64_t)(it.split + 1) * nk / sk.ways);
+  return it;
+}
+
 // kQuant: NVFP4 output (out.codes, out.scales, out.tensor_scale) instead of
-// bf16 (out.y, out.y_amax); whole tiles only.
+// bf16 (out.y, out.y_amax); whole tiles only, one per workgroup.
+// Persistent: workgroup b takes work items b, b + gridDim.x, ... below
+// `items` (the grid is a multiple of the 8 XCDs, so every item of a
+// workgroup maps to its XCD's range of the tile order, as a one-item launch
+// would).  Stage t of an item lives in slot (t + 2) % 3, so its first stage
+// lands in slot 2, which the epilogue's staging (the first 64 KB) leaves
+// alone: the next item's first stage is loaded while this item's epilogue
+// runs, and the next item starts with it in LDS.  The output amax is
+// carried across items and reduced once per workgroup.
 template <bool kQuant>
 __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ sa, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ sw,
     const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, int epi, Out out,
-    SplitK sk) {
+    SplitK sk, int64_t items) {
   // three stage slots: the loads of stage t + 2 are issued while stage t runs
   __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * kVStage];
   static_assert(4 * 16384 + 4 * 32 * 136 * 2 + 4 * 512 <= 3 * kVStage,
                 "epilogue staging and encode-factor tables fit in the stage ring");
+  static_assert(4 * 16384 <= 2 * kVStage, "the bf16 epilogue's staging leaves slot 2 free");
   __shared__ __attribute__((aligned(16))) float col_bias[kVBN];
+#define V5_SLOT(t) (lds + (((t) + 2) % 3) * kVStage)
   const int64_t tiles_m = (M + kVBM - 1) / kVBM, tiles_n = (N + kVBN - 1) / kVBN;
-  int64_t tm, tn, tail;
-  int split;
-  split_coords(tiles_m, tiles_n, sk, tm, tn, tail, split);
-  const int64_t m0 = tm * kVBM, n0 = tn * kVBN;
-  {
-    const int64_t c = n0 + threadIdx.x;
-    col_bias[threadIdx.x] = (bias && c < N) ? bf16_bits_to_f32(bias[c]) : 0.0f;
-  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, h = lane >> 5, x = (r >> 2) & 3;
   const int a_row = wm * kVWM + r, w_row = wn * kVWN + r;
-
-  V5Src src;
-  v5_setup(M, N, K, m0, n0, src);
-  f32x16 acc[kVTM][kVTN];
-#pragma unroll
-  for (int i = 0; i < kVTM; ++i)
-#pragma unroll
-    for (int j = 0; j < kVTN; ++j) acc[i][j] = f32x16{};
-
-  // stages [kb, ke) of 128 K: all of them, or this split's share
   const int nk = (int)(K / kVBK);
-  const int kb = split < 0 ? 0 : (int)((int64_t)split * nk / sk.ways);
-  const int ke = split < 0 ? nk : (int)((int64_t)(split + 1) * nk / sk.ways);
-  const int ns = ke - kb;
-  V5Packed p;
-  V5Ops oa, ob, oc;
-  // stage kb + t lives in slot t % 3
-  v5_issue(a_codes, a_scales, w_codes, w_scales, src, kb, lds);
-  if (ns > 1) v5_issue(a_codes, a_scales, w_codes, w_scales, src, kb + 1, lds + kVStage);
-  v5_barrier(ns > 1);
-  {
-    uint32_t sc[8];
-    v5_read(lds, a_row, w_row, h, x, p, sc);
-    if (ns > 2) v5_issue(a_codes, a_scales, w_codes, w_scales, src, kb + 2, lds + 2 * kVStage);
-    v5_scales(sc, p);
-  }
-  v5_decode<0>(p, oa);
-  v5_body(p, ob, oa, oc, acc);             // steps 6, 7 pending in oa, oc
-  // each stage leaves its step 6 in the set it decoded step 0 into; one copy
-  // per stage puts it back where the next stage expects it
-  for (int t = 1; t < ns; ++t) {
-    v5_stage(a_codes, a_scales, w_codes, w_scales, src, lds + (t % 3) * kVStage,
-             lds + ((t + 2) % 3) * kVStage, t + 1 < ns, t + 2 < ns, kb + t + 2, a_row, w_row, h, x,
-             p, ob, oa, oc, acc);
-    oa = ob;
-  }
-  v5_mfma(oa, acc);
-  v5_mfma(oc, acc);
+  const float scale = (*sa) * (*sw);
 
-  if (!kQuant && split >= 0) {
-    // a tail split: fp32 partial sums into its slice in accumulator order --
-    // float4 number (((wave * 4 + i) * 4 + j) * 64 + lane) * 4 + g holds
-    // acc[i][j][4g .. 4g+3], so each wave writes 4 KB contiguous per tile
-    f32x4* slice = reinterpret_cast<f32x4*>(sk.part + (tail * sk.ways + split) * (int64_t)(kVBM * kVBN));
+  int64_t b = blockIdx.x;
+  V5Item it = v5_item(b, tiles_m, tiles_n, sk, nk);
+  V5Src src;
+  v5_setup(M, N, K, it.m0, it.n0, src);
+  v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb, V5_SLOT(0));
+  u16x2 amax = {0, 0};
+  for (;;) {
+    {
+      const int64_t c = it.n0 + threadIdx.x;
+      col_bias[threadIdx.x] = (bias && c < N) ? bf16_bits_to_f32(bias[c]) : 0.0f;
+    }
+    f32x16 acc[kVTM][kVTN];
 #pragma unroll
     for (int i = 0; i < kVTM; ++i)
 #pragma unroll
-      for (int j = 0; j < kVTN; ++j)
+      for (int j = 0; j < kVTN; ++j) acc[i][j] = f32x16{};
+
+    // stages [kb, ke) of 128 K: all of them, or this split's share; the
+    // first one is already issued
+    const int ns = it.ke - it.kb;
+    V5Packed p;
+    V5Ops oa, ob, oc;
+    if (ns > 1) v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb + 1, V5_SLOT(1));
+    v5_barrier(ns > 1);
+    {
+      uint32_t sc[8];
+      v5_read(V5_SLOT(0), a_row, w_row, h, x, p, sc);
+      if (ns > 2) v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb + 2, V5_SLOT(2));
+      v5_scales(sc, p);
+    }
+    v5_decode<0>(p, oa);
+    v5_body(p, ob, oa, oc, acc);             // steps 6, 7 pending in oa, oc
+    // each stage leaves its step 6 in the set it decoded step 0 into; one copy
+    // per stage puts it back where the next stage expects it
+    for (int t = 1; t < ns; ++t) {
+      v5_stage(a_codes, a_scales, w_codes, w_scales, src, V5_SLOT(t), V5_SLOT(t + 2), t + 1 < ns,
+               t + 2 < ns, it.kb + t + 2, a_row, w_row, h, x, p, ob, oa, oc, acc);
+      oa = ob;
+    }
+    v5_mfma(oa, acc);
+    v5_mfma(oc, acc);
+
+    const V5Item cur = it;
+    const int64_t nb = b + gridDim.x;
+    const bool has_next = nb < items;
+    if (!kQuant && cur.split >= 0) {
+      // a tail split: fp32 partial sums into its slice in accumulator order --
+      // float4 number (((wave * 4 + i) * 4 + j) * 64 + lane) * 4 + g holds
+      // acc[i][j][4g .. 4g+3], so each wave writes 4 KB contiguous per tile
+      f32x4* slice =
+          reinterpret_cast<f32x4*>(sk.part + (cur.tail * sk.ways + cur.split) * (int64_t)(kVBM * kVBN));
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          slice[(((wave * kVTM + i) * kVTN + j) * 64 + lane) * 4 + g] =
-              f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-    return;
+      for (int i = 0; i < kVTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kVTN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            slice[(((wave * kVTM + i) * kVTN + j) * 64 + lane) * 4 + g] =
+                f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+      if (!has_next) break;
+      asm volatile("s_barrier" ::: "memory");   // every wave is done reading this item's slots
+      b = nb;
+      it = v5_item(b, tiles_m, tiles_n, sk, nk);
+      v5_setup(M, N, K, it.m0, it.n0, src);
+      v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb, V5_SLOT(0));
+      continue;
+    }
+    __syncthreads();   // every wave is done with the stage buffers
+    if (has_next) {    // the next item's first stage, into slot 2, under the epilogue
+      b = nb;
+      it = v5_item(b, tiles_m, tiles_n, sk, nk);
+      v5_setup(M, N, K, it.m0, it.n0, src);
+      v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb, V5_SLOT(0));
+    }
+    float* st = reinterpret_cast<float*>(lds + wave * 16384);
+    if (kQuant)   // bf16 staging after the four fp32 areas: 32 rows of 136 halves per wave
+      v5_epilogue_quant(acc, scale, col_bias, epi, M, N, cur.m0, cur.n0, out, st,
+                        reinterpret_cast<uint16_t*>(lds + 4 * 16384 + wave * 32 * 136 * 2),
+                        reinterpret_cast<float*>(lds + 4 * 16384 + 4 * 32 * 136 * 2 + wave * 512));
+    else
+      amax = max_u16x2(amax, v5_epilogue(acc, scale, col_bias, epi, M, N, cur.m0, cur.n0, out.y, st));
+    if (!has_next) break;
+    // every wave is done with the epilogue's staging and col_bias before the
+    // next item's loads refill slots 0 and 1 and its bias is written
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
   }
-  __syncthreads();   // every wave is done with the stage buffers
-  float* st = reinterpret_cast<float*>(lds + wave * 16384);
-  if (kQuant)   // bf16 staging after the four fp32 areas: 32 rows of 136 halves per wave
-    v5_epilogue_quant(acc, (*sa) * (*sw), col_bias, epi, M, N, m0, n0, out, st,
-                      reinterpret_cast<uint16_t*>(lds + 4 * 16384 + wave * 32 * 136 * 2),
-                      reinterpret_cast<float*>(lds + 4 * 16384 + 4 * 32 * 136 * 2 + wave * 512));
-  else
-    v5_epilogue(acc, (*sa) * (*sw), col_bias, epi, M, N, m0, n0, out.y, out.y_amax, st);
+#undef V5_SLOT
+  if (!kQuant && out.y_amax) {   // one atomic per workgroup
+    __shared__ uint32_t wave_amax[kVNT / 64];
+    uint32_t a = (uint32_t)(amax.x > amax.y ? amax.x : amax.y) << 16;
+    a = wave_max_u32(a);
+    if (lane == 0) wave_amax[wave] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int w = 0; w < kVNT / 64; ++w) m = max(m, wave_amax[w]);
+      atomicMax(out.y_amax, m);
+    }
+  }
 }
 
 // Sums the slices of v5's tail tiles in split order and applies v5's epilogue
@@ -1509,16 +1560,24 @@ hipError_t launch_v5(const uint8_t* a_codes, const uint8_t* a_scales, const floa
   const bool split = plan.ways > 1 && workspace && workspace_bytes >= plan.bytes;
   const SplitK sk = split ? SplitK{static_cast<float*>(workspace), plan.main_tiles, plan.ways}
                           : SplitK{nullptr, plan.tiles, 1};
-  const int64_t grid = split ? plan.main_tiles + plan.tail * plan.ways : plan.tiles;
+  const int64_t items = split ? plan.main_tiles + plan.tail * plan.ways : plan.tiles;
   const uint16_t* b16 = reinterpret_cast<const uint16_t*>(bias);
-  if (out.codes) {   // NVFP4 output: whole tiles
+  if (out.codes) {   // NVFP4 output: whole tiles, one per workgroup
     const SplitK whole{nullptr, plan.tiles, 1};
     hipLaunchKernelGGL(gemm_nvfp4_v5_kernel<true>, dim3((unsigned)plan.tiles), dim3(kVNT), 0, stream,
-                       a_codes, a_scales, sa, w_codes, w_scales, sw, b16, M, N, K, epi, out, whole);
+                       a_codes, a_scales, sa, w_codes, w_scales, sw, b16, M, N, K, epi, out, whole,
+                       plan.tiles);
     return hipGetLastError();
   }
+  // persistent grid, one workgroup per compute unit, when there are more
+  // items than compute units and the units divide into whole XCD groups
+  // (NVFP4_GEMM_PERSISTENT=0: one item per workgroup)
+  const int cus = compute_units();
+  const char* pe = getenv("NVFP4_GEMM_PERSISTENT");
+  const bool persistent = items > cus && cus % kXcds == 0 && !(pe && strcmp(pe, "0") == 0);
+  const int64_t grid = persistent ? cus : items;
   hipLaunchKernelGGL(gemm_nvfp4_v5_kernel<false>, dim3((unsigned)grid), dim3(kVNT), 0, stream, a_codes,
-                     a_scales, sa, w_codes, w_scales, sw, b16, M, N, K, epi, out, sk);
+                     a_scales, sa, w_codes, w_scales, sw, b16, M, N, K, epi, out, sk, items);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   hipLaunchKernelGGL(v5_split_reduce_kernel, dim3((unsigned)(plan.tail * kV5ReduceWgs)), dim3(256), 0,
