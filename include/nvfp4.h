@@ -334,6 +334,33 @@ int nvfp4_gemm_bf16(const void* x_bf16, const void* w_bf16, const void* bias_bf1
                     void* stream);
 
 /*
+ * Graph capture of a sequence of library calls.  [P1] section "CUDA Graphs"
+ * runs the DiT forward pass as one graph launch instead of one launch per
+ * kernel; these four calls do the same with HIP graphs for any sequence of
+ * this library's calls (every kernel here is capture-safe: no memset nodes,
+ * flags and counters are cleared or kept consistent by kernels).
+ *
+ * nvfp4_graph_begin  starts capturing what later calls enqueue on `stream`
+ *                    (a stream the caller created; the null stream cannot be
+ *                    captured).  Thread-local capture: other threads' HIP
+ *                    calls are unaffected; this thread must not allocate
+ *                    device memory until nvfp4_graph_end.
+ * nvfp4_graph_end    ends the capture on `stream` and instantiates it;
+ *                    *graph receives an opaque handle.
+ * nvfp4_graph_launch enqueues the captured kernels on `stream` (any stream),
+ *                    with the pointers and sizes they were captured with:
+ *                    refresh inputs in place between launches.
+ * nvfp4_graph_destroy releases the handle.
+ * Returns NVFP4_ERR_NULL for a NULL stream (begin / end) or graph, else
+ * NVFP4_OK or NVFP4_ERR_HIP (capture or instantiation failed; a failed
+ * nvfp4_graph_end leaves no capture running).
+ */
+int nvfp4_graph_begin(void* stream);
+int nvfp4_graph_end(void* stream, void** graph);
+int nvfp4_graph_launch(void* graph, void* stream);
+int nvfp4_graph_destroy(void* graph);
+
+/*
  * nvfp4_layer_is_quantized -- the exclude-pattern predicate of [P1]
  * "NVFP4量化".  Host only; touches no device.
  *   layer_name  NUL-terminated module path, e.g. "transformer_blocks.0.attn.to_q".

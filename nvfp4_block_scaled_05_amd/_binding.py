@@ -39,6 +39,10 @@ SIGNATURES = {
     "nvfp4_fp8_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P,
                                       ctypes.c_size_t, _P]),
     "nvfp4_fp8_gemm_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
+    "nvfp4_graph_begin": (ctypes.c_int, [_P]),
+    "nvfp4_graph_end": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_void_p)]),
+    "nvfp4_graph_launch": (ctypes.c_int, [_P, _P]),
+    "nvfp4_graph_destroy": (ctypes.c_int, [_P]),
     "nvfp4_layer_is_quantized": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_char_p]),
 }
 

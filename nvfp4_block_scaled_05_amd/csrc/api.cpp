@@ -251,6 +251,38 @@ int nvfp4_gemm_bf16(const void* x_bf16, const void* w_bf16, const void* bias_bf1
                                             static_cast<hipStream_t>(stream)));
 }
 
+int nvfp4_graph_begin(void* stream) {
+  if (!stream) return NVFP4_ERR_NULL;
+  int st = check_device();
+  if (st != NVFP4_OK) return st;
+  return hip_status(
+      hipStreamBeginCapture(static_cast<hipStream_t>(stream), hipStreamCaptureModeThreadLocal));
+}
+
+int nvfp4_graph_end(void* stream, void** graph) {
+  if (!stream || !graph) return NVFP4_ERR_NULL;
+  hipGraph_t g = nullptr;
+  if (hipStreamEndCapture(static_cast<hipStream_t>(stream), &g) != hipSuccess || !g)
+    return NVFP4_ERR_HIP;
+  hipGraphExec_t exec = nullptr;
+  const hipError_t e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+  hipGraphDestroy(g);
+  if (e != hipSuccess) return NVFP4_ERR_HIP;
+  *graph = exec;
+  return NVFP4_OK;
+}
+
+int nvfp4_graph_launch(void* graph, void* stream) {
+  if (!graph) return NVFP4_ERR_NULL;
+  return hip_status(
+      hipGraphLaunch(static_cast<hipGraphExec_t>(graph), static_cast<hipStream_t>(stream)));
+}
+
+int nvfp4_graph_destroy(void* graph) {
+  if (!graph) return NVFP4_ERR_NULL;
+  return hip_status(hipGraphExecDestroy(static_cast<hipGraphExec_t>(graph)));
+}
+
 int nvfp4_layer_is_quantized(const char* layer_name, const char* pattern) {
   if (!layer_name) return NVFP4_ERR_NULL;
   try {

@@ -51,7 +51,7 @@ def test_public_include_holds_only_the_library_header():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
         assert n in _binding.SIGNATURES, n
@@ -208,6 +208,18 @@ def test_fp8_gemm_workspace_bytes(lib):
     # MLP up: 96 tiles past 12 rounds would split only 2 ways: whole
     assert wb(16896, 12288, 3072) == 0
     assert wb(256 * 16, 256 * 16, 4096) == 0        # whole rounds only
+
+
+def test_graph_argument_errors(lib):
+    import ctypes
+    h = ctypes.c_void_p()
+    assert lib.nvfp4_graph_begin(None) == NULL          # the null stream cannot be captured
+    assert lib.nvfp4_graph_end(None, ctypes.byref(h)) == NULL
+    assert lib.nvfp4_graph_end(A, None) == NULL
+    assert lib.nvfp4_graph_launch(None, None) == NULL
+    assert lib.nvfp4_graph_destroy(None) == NULL
+    if not _has_gfx950():
+        assert lib.nvfp4_graph_begin(A) == DEVICE
 
 
 def test_layer_predicate_matches_python_re(lib):
