@@ -30,6 +30,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --summarize-trace kernel_trace.csv [--trace-json out.json]
                                          (per-kernel, per-grid durations of a rocprofv3
                                           --kernel-trace CSV; no GPU needed)
+       python bench.py --summarize-counters counter_collection.csv
+                                         (per-kernel means of a rocprofv3 --pmc CSV)
+       (both take the profiled run's --steps / --warmup to find its timed GEMMs)
 """
 
 import argparse
@@ -71,6 +74,8 @@ def parse():
                    help="summarize a rocprofv3 kernel_trace.csv and exit")
     p.add_argument("--trace-json", metavar="JSON", help="with --summarize-trace: also write JSON")
     p.add_argument("--trace-command", default="", help="with --trace-json: the profiled command")
+    p.add_argument("--summarize-counters", metavar="CSV",
+                   help="summarize a rocprofv3 --pmc counter_collection.csv and exit (JSON)")
     return p.parse_args()
 
 
@@ -138,59 +143,113 @@ def _short_kernel_name(name):
     return base[last:].strip()
 
 
-def summarize_trace(csv_path):
+def summarize_trace(csv_path, warmup, steps):
     """Per (kernel, grid size) dispatch statistics of a rocprofv3
-    --kernel-trace CSV: launches, mean / median / min / max duration in us."""
+    --kernel-trace CSV of this script (launches, mean / median / min / max
+    duration in us), and the headline step's two GEMMs on their own: the
+    v5 kernel's launches come first in the run, as [up, down] once while the
+    step's buffers are set up, `warmup` times, then `steps` timed times, so
+    the timed up and down launches are picked by their index."""
     import csv
-    groups = {}
+    groups, v5 = {}, []
     with open(csv_path, newline="") as f:
-        for row in csv.DictReader(f):
-            name = _short_kernel_name(row.get("Kernel_Name", ""))
-            grid = row.get("Grid_Size_X") or row.get("Grid_Size") or "0"
-            wg = row.get("Workgroup_Size_X") or row.get("Workgroup_Size") or "1"
-            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
-            key = (name, int(grid) // max(int(wg), 1))
-            groups.setdefault(key, []).append(dur)
-    out = []
-    for (name, wgs), d in groups.items():
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    for row in rows:
+        name = _short_kernel_name(row.get("Kernel_Name", ""))
+        grid = row.get("Grid_Size_X") or row.get("Grid_Size") or "0"
+        wg = row.get("Workgroup_Size_X") or row.get("Workgroup_Size") or "1"
+        dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+        groups.setdefault((name, int(grid) // max(int(wg), 1)), []).append(dur)
+        if name == "gemm_nvfp4_v5_kernel<false>":
+            v5.append(dur)
+
+    def stats(d):
         a = np.array(d)
-        out.append({"kernel": name, "workgroups": wgs, "launches": len(d),
-                    "avg_us": round(float(a.mean()), 2), "median_us": round(float(np.median(a)), 2),
-                    "min_us": round(float(a.min()), 2), "max_us": round(float(a.max()), 2),
-                    "total_us": round(float(a.sum()), 1)})
+        return {"launches": len(d), "avg_us": round(float(a.mean()), 2),
+                "median_us": round(float(np.median(a)), 2), "min_us": round(float(a.min()), 2),
+                "max_us": round(float(a.max()), 2), "total_us": round(float(a.sum()), 1)}
+    out = [{"kernel": name, "workgroups": wgs, **stats(d)} for (name, wgs), d in groups.items()]
     out.sort(key=lambda r: -r["total_us"])
-    return out
+    first = 2 * (1 + warmup)
+    headline = None
+    if len(v5) >= first + 2 * steps:
+        headline = {"gemm_up_gelu_amax": stats(v5[first:first + 2 * steps:2]),
+                    "gemm_down": stats(v5[first + 1:first + 2 * steps:2]),
+                    "selection": f"gemm_nvfp4_v5_kernel<false> launches {first}, {first + 2}, ... "
+                                 f"(up) and {first + 1}, {first + 3}, ... (down): the {steps} timed "
+                                 f"steps after {warmup} warm-up steps and the setup call"}
+    return out, headline
 
 
-def print_trace_summary(rows, source_hash, command, json_path=None):
+def print_trace_summary(rows, headline, source_hash, command, json_path=None):
     print("| kernel | workgroups | launches | average us | median us | min us | max us |")
     print("|---|---|---|---|---|---|---|")
     for r in rows:
         print(f"| {r['kernel']} | {r['workgroups']} | {r['launches']} | {r['avg_us']} | "
               f"{r['median_us']} | {r['min_us']} | {r['max_us']} |")
+    if headline:
+        print()
+        print("| headline step kernel | launches | average us | median us | min us | max us |")
+        print("|---|---|---|---|---|---|")
+        for k in ("gemm_up_gelu_amax", "gemm_down"):
+            r = headline[k]
+            print(f"| {k} | {r['launches']} | {r['avg_us']} | {r['median_us']} | {r['min_us']} | "
+                  f"{r['max_us']} |")
     if json_path:
         with open(json_path, "w") as f:
-            json.dump({"source_hash": source_hash, "command": command, "dispatches": rows}, f,
-                      indent=1)
+            json.dump({"source_hash": source_hash, "command": command, "headline": headline,
+                       "dispatches": rows}, f, indent=1)
             f.write("\n")
 
 
+def summarize_counters(csv_path, warmup, steps):
+    """Per (kernel, grid size) mean of every counter in a rocprofv3 --pmc
+    counter_collection CSV of this script, and the same for the headline
+    step's up and down GEMMs, picked by launch index as in summarize_trace."""
+    import csv
+    disp = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            d = disp.setdefault(int(row["Dispatch_Id"]), {
+                "kernel": _short_kernel_name(row.get("Kernel_Name", "")),
+                "workgroups": int(row.get("Grid_Size") or 0) // max(int(row.get("Workgroup_Size") or 1), 1),
+                "counters": {}})
+            name = row["Counter_Name"]
+            d["counters"][name] = d["counters"].get(name, 0.0) + float(row["Counter_Value"])
+    order = [disp[k] for k in sorted(disp)]
+
+    def mean(ds):
+        names = sorted({n for d in ds for n in d["counters"]})
+        return {"launches": len(ds),
+                **{n: float(np.mean([d["counters"].get(n, 0.0) for d in ds])) for n in names}}
+    groups = {}
+    for d in order:
+        groups.setdefault((d["kernel"], d["workgroups"]), []).append(d)
+    rows = [{"kernel": k, "workgroups": w, **mean(ds)} for (k, w), ds in groups.items()]
+    v5 = [d for d in order if d["kernel"] == "gemm_nvfp4_v5_kernel<false>"]
+    first = 2 * (1 + warmup)
+    headline = None
+    if len(v5) >= first + 2 * steps:
+        headline = {"gemm_up_gelu_amax": mean(v5[first:first + 2 * steps:2]),
+                    "gemm_down": mean(v5[first + 1:first + 2 * steps:2])}
+    return rows, headline
+
+
 def profiled_up_gemm():
-    """The up GEMM's average duration in the committed kernel trace of the
-    bench command, if that trace was taken on the current kernel sources."""
+    """The up GEMM's average duration over the timed steps in the committed
+    kernel trace of this command, if that trace was taken on the current
+    kernel sources."""
     path = os.path.join(ROOT, "profiles", "dit_mlp_2048_kernel_trace.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash() or not rec.get("headline"):
         return None
-    for r in rec.get("dispatches", []):
-        if r["kernel"].startswith("gemm_nvfp4_v5_kernel<false>") and r["workgroups"] == UP_TILES:
-            return {"avg_launch_us": r["avg_us"], "median_us": r["median_us"],
-                    "launches": r["launches"], "command": rec.get("command", "")}
-    return None
+    r = rec["headline"]["gemm_up_gelu_amax"]
+    return {"avg_launch_us": r["avg_us"], "median_us": r["median_us"], "launches": r["launches"],
+            "command": rec.get("command", "")}
 
 
 def calibration(ev, stream):
@@ -252,9 +311,15 @@ def calibration(ev, stream):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        rows, headline = summarize_counters(args.summarize_counters, args.warmup, args.steps)
+        print(json.dumps({"source_hash": kernel_source_hash(), "headline": headline,
+                          "dispatches": rows}, indent=1))
+        return
     if args.summarize_trace:
-        print_trace_summary(summarize_trace(args.summarize_trace), kernel_source_hash(),
-                            args.trace_command, args.trace_json)
+        rows, headline = summarize_trace(args.summarize_trace, args.warmup, args.steps)
+        print_trace_summary(rows, headline, kernel_source_hash(), args.trace_command,
+                            args.trace_json)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
