@@ -368,7 +368,11 @@ int nvfp4_graph_destroy(void* graph);
  *               pattern ^(?!.*(embedder|norm_out|proj_out|to_add_out|to_added_qkv|stream)).*
  * Returns 1 when the pattern matches a prefix of the name (the layer runs in
  * NVFP4), 0 when it does not (the layer stays bf16), NVFP4_ERR_NULL for a NULL
- * name, NVFP4_ERR_ARG for a pattern that does not compile.
+ * name, NVFP4_ERR_ARG for a pattern that does not compile or, with a pattern
+ * given, a name longer than 1024 bytes (the regex engine's recursion grows
+ * with the name).  The default pattern is evaluated as the substring search it
+ * amounts to (none of the six words before the name's first \n or \r), for
+ * names of any length.
  */
 int nvfp4_layer_is_quantized(const char* layer_name, const char* pattern);
 

@@ -11,7 +11,9 @@ import os
 import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "lib", "libnvfp4.so")
+# NVFP4_LIBRARY names another build of the same sources (the host-sanitizer
+# build of the tests); by default the in-tree library.
+LIB_PATH = os.environ.get("NVFP4_LIBRARY") or os.path.join(PKG, "lib", "libnvfp4.so")
 
 NVFP4_OK = 0
 STATUS_NAMES = {0: "NVFP4_OK", -1: "NVFP4_ERR_NULL", -2: "NVFP4_ERR_SHAPE",

@@ -31,7 +31,21 @@ DEVICE_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-ffp-contract=off",
     "-I", INCLUDE, "-Wall", "-Wno-unused-function",
 ]
-HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-I", INCLUDE, "-Wall"]
+# api.cpp holds no device code: compiled for the host only
+HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "--cuda-host-only", "-I", INCLUDE, "-Wall"]
+
+# The host-sanitizer build of the tests: the library's host code (argument
+# checks, the layer predicate, launch set-up) under AddressSanitizer and
+# UndefinedBehaviorSanitizer, each -fsanitize= behind -Xarch_host so no device
+# code is instrumented.  Device code is compiled unoptimized: this build only
+# runs where no GPU is present, so its kernels never execute.
+SANITIZE_FLAGS = [
+    "--offload-arch=gfx950", "-O1", "-Xarch_device", "-O0", "-fPIC", "-std=c++17",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+    "-I", INCLUDE,
+]
 
 SOURCES = ["quantize.hip", "gemm_nvfp4.hip", "gemm.hip", "fp8.hip", "api.cpp"]
 # test-only library: conversion probes and the calibration kernels of the
@@ -76,6 +90,46 @@ def _link(target, objs):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, target)
+
+
+def asan_runtime():
+    """Path of the AddressSanitizer runtime a process must preload to load the
+    sanitizer build."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin",
+                         "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return path
+
+
+def build_host_sanitized(outdir):
+    """Build the library's sources with the sanitizer flags into
+    ``outdir/libnvfp4_sanitized.so`` and return its path."""
+    os.makedirs(outdir, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(outdir, src + ".o")
+        cmd = [HIPCC, *SANITIZE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitizer build failed for {src}:\n{r.stdout}{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    target = os.path.join(outdir, "libnvfp4_sanitized.so")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-shared-libsan",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-o", target] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitizer link failed:\n" + r.stdout + r.stderr)
+    return target
 
 
 def clean():

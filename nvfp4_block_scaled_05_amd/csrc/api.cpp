@@ -11,6 +11,7 @@
 #include <cstring>
 #include <regex>
 #include <string>
+#include <string_view>
 
 #include "kernels.hpp"
 #include "nvfp4.h"
@@ -42,8 +43,25 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP
 
 bool bad_dim(int64_t v) { return v < 0 || v >= kMaxDim; }
 
-constexpr const char* kPagePattern =
-    "^(?!.*(embedder|norm_out|proj_out|to_add_out|to_added_qkv|stream)).*";
+// The page's exclude pattern, ^(?!.*(embedder|norm_out|proj_out|to_add_out|
+// to_added_qkv|stream)).*, matched from the start of the name: the lookahead
+// fails exactly when one of these words occurs before the name's first line
+// terminator (the pattern's `.` stops at \n and \r).  Evaluated as that
+// substring search, so a name of any length costs one linear scan.
+constexpr const char* kExcludedWords[] = {"embedder", "norm_out",     "proj_out",
+                                          "to_add_out", "to_added_qkv", "stream"};
+
+int page_pattern_matches(const char* name) {
+  std::string_view s(name);
+  s = s.substr(0, s.find_first_of("\n\r"));
+  for (const char* w : kExcludedWords)
+    if (s.find(w) != std::string_view::npos) return 0;
+  return 1;
+}
+
+// The regex engine recurses once per character of the subject, so a caller's
+// pattern is only applied to names up to this length.
+constexpr size_t kMaxPatternName = 1024;
 
 }  // namespace
 
@@ -266,7 +284,8 @@ int nvfp4_graph_end(void* stream, void** graph) {
     return NVFP4_ERR_HIP;
   hipGraphExec_t exec = nullptr;
   const hipError_t e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
-  hipGraphDestroy(g);
+  // the instantiated graph does not need the captured one
+  static_cast<void>(hipGraphDestroy(g));
   if (e != hipSuccess) return NVFP4_ERR_HIP;
   *graph = exec;
   return NVFP4_OK;
@@ -285,16 +304,12 @@ int nvfp4_graph_destroy(void* graph) {
 
 int nvfp4_layer_is_quantized(const char* layer_name, const char* pattern) {
   if (!layer_name) return NVFP4_ERR_NULL;
+  if (!pattern) return page_pattern_matches(layer_name);
   try {
-    static const std::regex page_re(kPagePattern, std::regex::ECMAScript);
-    std::regex custom;
-    const std::regex* re = &page_re;
-    if (pattern) {
-      custom = std::regex(pattern, std::regex::ECMAScript);
-      re = &custom;
-    }
+    const std::regex re(pattern, std::regex::ECMAScript);
     const std::string name(layer_name);
-    return std::regex_search(name, *re, std::regex_constants::match_continuous) ? 1 : 0;
+    if (name.size() > kMaxPatternName) return NVFP4_ERR_ARG;
+    return std::regex_search(name, re, std::regex_constants::match_continuous) ? 1 : 0;
   } catch (const std::exception&) {
     return NVFP4_ERR_ARG;
   }

@@ -232,6 +232,37 @@ def test_layer_predicate_matches_python_re(lib):
     assert lib.nvfp4_layer_is_quantized(b"x.blocks", b"blocks") == 0   # match at the start only
 
 
+PAGE_PATTERN = b"^(?!.*(embedder|norm_out|proj_out|to_add_out|to_added_qkv|stream)).*"
+
+
+def test_layer_predicate_default_is_the_page_regex(lib):
+    # the default pattern is evaluated as a substring search; the same names
+    # through the regex engine with the page's pattern spelled out must agree,
+    # including the line-terminator edge (the pattern's `.` stops at \n, \r)
+    from tests.test_oracle_layers import load_golden
+    names = [n.encode() for n, _ in load_golden()] + [
+        b"", b"norm_out", b"a.norm_out.b", b"norm_ou", b"to_add_outx", b"to_added_qk",
+        b"to_added_qkv", b"x_embedder", b"upstream", b"proj_out.0", b"a\nnorm_out",
+        b"a\rstream", b"stream\nx", b"a\n\rembedder", b"ab\xe2\x80\xa8proj_out",
+        b"\xff\xfe.to_add_out", b"st\nream",
+    ]
+    for n in names:
+        want = lib.nvfp4_layer_is_quantized(n, PAGE_PATTERN)
+        assert want in (0, 1), n
+        assert lib.nvfp4_layer_is_quantized(n, None) == want, n
+
+
+def test_layer_predicate_long_names(lib):
+    # the default pattern takes names of any length (one linear scan); a
+    # caller's pattern is applied to names up to 1024 bytes
+    f = lib.nvfp4_layer_is_quantized
+    assert f(b"a" * 200_000, None) == 1
+    assert f(b"a" * 200_000 + b".norm_out", None) == 0
+    assert f(b"b" * 1024, b"b*") == 1
+    assert f(b"b" * 1025, b"b*") == ARG
+    assert f(b"b" * 1025, b"(unclosed") == ARG
+
+
 def _has_gfx950():
     try:
         import torch
