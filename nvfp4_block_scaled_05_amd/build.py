@@ -47,7 +47,8 @@ SANITIZE_FLAGS = [
     "-I", INCLUDE,
 ]
 
-SOURCES = ["quantize.hip", "gemm_nvfp4.hip", "gemm.hip", "fp8.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm_nvfp4.hip", "gemm_nvfp4_quant.hip", "gemm.hip", "fp8.hip",
+           "api.cpp"]
 # test-only library: conversion probes and the calibration kernels of the
 # roofline measurement (isa_probe.h, calib.h beside the sources)
 PROBE_SOURCES = ["isa_probe.hip", "calib.hip"]
@@ -72,7 +73,7 @@ def build(verbose=False):
     os.makedirs(OBJDIR, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     srcs = SOURCES + PROBE_SOURCES
-    with ThreadPoolExecutor(max_workers=min(5, len(srcs))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         results = dict(zip(srcs, ex.map(_compile, srcs)))
     if verbose:
         for src, (_, out) in results.items():
