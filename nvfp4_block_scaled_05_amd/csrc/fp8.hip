@@ -381,31 +381,30 @@ __device__ __forceinline__ void dma_barrier() {
   __syncthreads();
 }
 
-// One stage: refill `nxt` with the stage after this one (if any), read this
+// One stage: refill `nxt` with the stage after this one (REFILL), read this
 // stage's fragments from `cur`, and run the previous stage's second k-step and
 // this stage's first.  MFMAs are interleaved with the LDS reads and the DMA
-// issues so that the reads' latency is covered by matrix work.
+// issues, one load per MFMA over the first half of the stage: early enough to
+// land before the next barrier (two buffers leave one stage of latency), and
+// not in a burst, which would hold the matrix pipe idle while the compute
+// unit's address unit takes the loads.  REFILL is compile-time so that the
+// loads sit in the MFMAs' basic block instead of a branch of their own.
+template <bool REFILL>
 __device__ __forceinline__ void dma_stage(const uint8_t* __restrict__ a, const uint8_t* __restrict__ w,
                                           const uint8_t* cur, uint8_t* nxt, const DmaPtrs& ptr,
-                                          bool refill, int64_t k_next, int a_off, int b_off, int h,
-                                          int sw, DmaFrags& f0, DmaFrags& f1,
-                                          f32x16 (&acc)[kDTM][kDTN]) {
+                                          int64_t k_next, int a_off, int b_off, int h, int sw,
+                                          DmaFrags& f0, DmaFrags& f1, f32x16 (&acc)[kDTM][kDTN]) {
   dma_barrier();
-  if (refill) dma_issue(a, w, ptr, k_next, nxt);
+  if (REFILL) dma_issue(a, w, ptr, k_next, nxt);
   dma_frags<0>(cur, a_off, b_off, h, sw, f0);
   dma_mfma(f1, acc);                        // previous stage, k-step 1
   dma_frags<1>(cur, a_off, b_off, h, sw, f1);
   dma_mfma(f0, acc);
 #pragma unroll
-  for (int m = 0; m < kDTM * kDTN; ++m) {
+  for (int m = 0; m < 2 * kDTM * kDTN; ++m) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (DMA issue)
-  }
-#pragma unroll
-  for (int m = 0; m < kDTM * kDTN; ++m) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (REFILL && m < kDTM * kDTN) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (DMA issue)
   }
 }
 
@@ -498,16 +497,21 @@ __global__ __launch_bounds__(kDNT, 1) void gemm_fp8_dma_kernel(
   dma_mfma(f0, acc);
   // stage kb + t reads buffer t % 2 and refills the other with stage kb + t + 1;
   // whole pairs of stages, then at most one more
+  // whole pairs of stages, then at most one more.  Both stages of a pair
+  // load: the second stage of the last pair, with no stage left to load,
+  // loads its own stage again into the buffer nothing reads any more (a
+  // branch around its loads would take them out of the MFMAs' basic block);
+  // those loads are waited for before the epilogue or the partial stores.
   int t = 1;
   for (; t + 1 < ns; t += 2) {
-    dma_stage(a, w, lds1, lds0, ptr, true, (int64_t)(kb + t + 1) * kDBK, a_off, b_off, h, sw, f0,
-              f1, acc);
-    dma_stage(a, w, lds0, lds1, ptr, t + 2 < ns, (int64_t)(kb + t + 2) * kDBK, a_off, b_off, h, sw,
-              f0, f1, acc);
+    dma_stage<true>(a, w, lds1, lds0, ptr, (int64_t)(kb + t + 1) * kDBK, a_off, b_off, h, sw, f0, f1,
+                    acc);
+    const int k2 = t + 2 < ns ? kb + t + 2 : kb + t + 1;
+    dma_stage<true>(a, w, lds0, lds1, ptr, (int64_t)k2 * kDBK, a_off, b_off, h, sw, f0, f1, acc);
   }
-  if (t < ns)
-    dma_stage(a, w, lds1, lds0, ptr, false, 0, a_off, b_off, h, sw, f0, f1, acc);
+  if (t < ns) dma_stage<false>(a, w, lds1, lds0, ptr, 0, a_off, b_off, h, sw, f0, f1, acc);
   dma_mfma(f1, acc);
+  __builtin_amdgcn_s_waitcnt(0);           // every load into LDS has landed
 
   if (split >= 0) {
     // a tail split: fp32 partial sums into its slice in accumulator order --
