@@ -332,16 +332,18 @@ __device__ __forceinline__ void bdma_barrier() {
   __syncthreads();
 }
 
-// One stage: refill `nxt` with the stage after this one (if any), read this
+// One stage: refill `nxt` with the stage after this one (REFILL), read this
 // stage's four k-steps from `cur` and run the previous stage's last k-step
 // and this stage's first three, MFMAs interleaved with the reads and loads.
+// REFILL is compile-time so that the loads sit in the MFMAs' basic block (a
+// branch around them issues them in a burst with the matrix pipe idle).
+template <bool REFILL>
 __device__ __forceinline__ void bdma_stage(const uint8_t* __restrict__ a, const uint8_t* __restrict__ w,
                                            const uint8_t* cur, uint8_t* nxt, const BDmaPtrs& ptr,
-                                           bool refill, int64_t kbyte_next, int a_off, int b_off,
-                                           int h, int sw, BFrags& f0, BFrags& f1,
-                                           f32x16 (&acc)[kETM][kETN]) {
+                                           int64_t kbyte_next, int a_off, int b_off, int h, int sw,
+                                           BFrags& f0, BFrags& f1, f32x16 (&acc)[kETM][kETN]) {
   bdma_barrier();
-  if (refill) bdma_issue(a, w, ptr, kbyte_next, nxt);
+  if (REFILL) bdma_issue(a, w, ptr, kbyte_next, nxt);
   bfrags<0>(cur, a_off, b_off, h, sw, f0);
   bmfma(f1, acc);                          // previous stage, k-step 3
   bfrags<1>(cur, a_off, b_off, h, sw, f1);
@@ -354,7 +356,7 @@ __device__ __forceinline__ void bdma_stage(const uint8_t* __restrict__ a, const 
   for (int m = 0; m < kETM * kETN; ++m) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (load issue)
+    if (REFILL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (load issue)
   }
 #pragma unroll
   for (int m = 0; m < 3 * kETM * kETN; ++m) {
@@ -442,15 +444,20 @@ __global__ __launch_bounds__(kENT, 1) void gemm_bf16_dma_kernel(
   bmfma(f0, acc);
   // stage t reads buffer t % 2 and refills the other with stage t + 1; whole
   // pairs of stages, then at most one more
+  // pairs of stages, then at most one more.  Both stages of a pair load: the
+  // second stage of the last pair, with no stage left, loads its own stage
+  // again into the buffer nothing reads any more; every load into LDS is
+  // waited for before the epilogue.
   int t = 1;
   for (; t + 1 < ns; t += 2) {
-    bdma_stage(x, w, lds1, lds0, ptr, true, (int64_t)(t + 1) * kERow, a_off, b_off, h, sw, f0, f1,
-               acc);
-    bdma_stage(x, w, lds0, lds1, ptr, t + 2 < ns, (int64_t)(t + 2) * kERow, a_off, b_off, h, sw, f0,
-               f1, acc);
+    bdma_stage<true>(x, w, lds1, lds0, ptr, (int64_t)(t + 1) * kERow, a_off, b_off, h, sw, f0, f1,
+                     acc);
+    const int t2 = t + 2 < ns ? t + 2 : t + 1;
+    bdma_stage<true>(x, w, lds0, lds1, ptr, (int64_t)t2 * kERow, a_off, b_off, h, sw, f0, f1, acc);
   }
-  if (t < ns) bdma_stage(x, w, lds1, lds0, ptr, false, 0, a_off, b_off, h, sw, f0, f1, acc);
+  if (t < ns) bdma_stage<false>(x, w, lds1, lds0, ptr, 0, a_off, b_off, h, sw, f0, f1, acc);
   bmfma(f1, acc);
+  __builtin_amdgcn_s_waitcnt(0);           // every load into LDS has landed
 
   // epilogue: acc + bias -> GELU -> bf16, the operations of gemm_bf16_kernel
   __syncthreads();   // every wave is done with the stage buffers
