@@ -222,6 +222,27 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
+// Global -> LDS load in the gfx950 buffer form: lane L's BYTES (4 or 16)
+// from base + lane_off + scalar_off land at lds + L * BYTES (lds is wave
+// uniform and goes through M0).  The 32-bit per-lane offset and the scalar
+// offset need no 64-bit address arithmetic per load.  The resource has record
+// count 0xFFFFFFFF (no range clamping: callers keep every offset inside the
+// buffer) and word 3 of the raw 32-bit data format used for untyped dword
+// access.
+constexpr int kBufferWord3 = 0x00020000;
+
+template <int BYTES>
+__device__ __forceinline__ void buffer_load_lds(const void* base, uint32_t lane_off, int scalar_off,
+                                                void* lds) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFF, kBufferWord3);
+  auto* dst = (__attribute__((address_space(3))) void*)lds;
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, lane_off, scalar_off, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, lane_off, scalar_off, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {

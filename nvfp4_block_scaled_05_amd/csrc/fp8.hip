@@ -324,13 +324,11 @@ __device__ __forceinline__ void dma_setup(int64_t M, int64_t N, int64_t K, int64
 __device__ __forceinline__ void dma_issue(const uint8_t* __restrict__ a, const uint8_t* __restrict__ w,
                                           const DmaPtrs& d, int64_t k0, uint8_t* stage) {
   const int wave = wave_id();
-  const uint8_t* ak = a + k0;
-  const uint8_t* wk = w + k0;
 #pragma unroll
   for (int i = 0; i < kDBM / 8 / 4; ++i) {
     const int c = wave * (kDBM / 8 / 4) + i;
-    __builtin_amdgcn_global_load_lds(ak + d.a[i], stage + c * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(wk + d.w[i], stage + kDOp + c * 1024, 16, 0, 0);
+    buffer_load_lds<16>(a, d.a[i], (int)k0, stage + c * 1024);
+    buffer_load_lds<16>(w, d.w[i], (int)k0, stage + kDOp + c * 1024);
   }
 }
 

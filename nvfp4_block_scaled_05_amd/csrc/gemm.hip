@@ -286,13 +286,11 @@ __device__ __forceinline__ void bdma_setup(int64_t M, int64_t N, int64_t K, int6
 __device__ __forceinline__ void bdma_issue(const uint8_t* __restrict__ a, const uint8_t* __restrict__ w,
                                            const BDmaPtrs& d, int64_t kbyte, uint8_t* stage) {
   const int wave = wave_id();
-  const uint8_t* ak = a + kbyte;
-  const uint8_t* wk = w + kbyte;
 #pragma unroll
   for (int i = 0; i < kEBM / 8 / 4; ++i) {
     const int c = wave * (kEBM / 8 / 4) + i;
-    __builtin_amdgcn_global_load_lds(ak + d.a[i], stage + c * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(wk + d.w[i], stage + kEOp + c * 1024, 16, 0, 0);
+    buffer_load_lds<16>(a, d.a[i], (int)kbyte, stage + c * 1024);
+    buffer_load_lds<16>(w, d.w[i], (int)kbyte, stage + kEOp + c * 1024);
   }
 }
 

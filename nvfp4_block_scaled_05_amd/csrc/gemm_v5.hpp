@@ -109,40 +109,17 @@ struct V5Refill {
   uint8_t* stage;
 };
 
-// A raw buffer resource over an operand: the gfx950 buffer form of the
-// global->LDS load takes a 32-bit per-lane offset and a scalar offset, so the
-// lane's row offset (V5Src) and the stage's K offset need no 64-bit address
-// arithmetic per load.  Record count 0xFFFFFFFF: no range clamping (every
-// offset here lies inside the operand, rows past M or N clamped to the last
-// one); word 3 is the raw 32-bit data format used for untyped dword access.
-constexpr int kBufferWord3 = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t v5_rsrc(const uint8_t* p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, (int)0xFFFFFFFF,
-                                           kBufferWord3);
-}
-
-template <int BYTES>
-__device__ __forceinline__ void v5_load_lds(const uint8_t* base, uint32_t lane_off, int stage_off,
-                                            uint8_t* lds) {
-  auto* dst = (__attribute__((address_space(3))) void*)lds;
-  if constexpr (BYTES == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(v5_rsrc(base), dst, 16, lane_off, stage_off, 0, 0);
-  else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(v5_rsrc(base), dst, 4, lane_off, stage_off, 0, 0);
-}
-
 template <int P>
 __device__ __forceinline__ void v5_issue_part(const V5Refill& r) {
   const int wave = wave_id();
   if constexpr (P < 4) {
     const int c = wave * 4 + P;
-    v5_load_lds<16>(r.ac, r.src->ac[P], r.kt * kVCodeRow, r.stage + kVA + c * 1024);
-    v5_load_lds<16>(r.wc, r.src->wc[P], r.kt * kVCodeRow, r.stage + kVW + c * 1024);
+    buffer_load_lds<16>(r.ac, r.src->ac[P], r.kt * kVCodeRow, r.stage + kVA + c * 1024);
+    buffer_load_lds<16>(r.wc, r.src->wc[P], r.kt * kVCodeRow, r.stage + kVW + c * 1024);
   } else {
     const int i = P - 4, c = wave * 2 + i;
-    v5_load_lds<4>(r.as, r.src->as[i], r.kt * kVScaleRow, r.stage + kVSA + c * 256);
-    v5_load_lds<4>(r.ws, r.src->ws[i], r.kt * kVScaleRow, r.stage + kVSW + c * 256);
+    buffer_load_lds<4>(r.as, r.src->as[i], r.kt * kVScaleRow, r.stage + kVSA + c * 256);
+    buffer_load_lds<4>(r.ws, r.src->ws[i], r.kt * kVScaleRow, r.stage + kVSW + c * 256);
   }
 }
 
