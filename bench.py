@@ -718,7 +718,36 @@ def yardstick_section(c):
         flop = 2 * m * n * k
         out[name] = {"shape": [m, n, k], "us": st["mm"], "TFLOPs": round(flop / (st["mm"] * 1e-6) / 1e12, 1)}
         del a, w, y
+    out["fp8"] = fp8_yardstick(c)
     return {"what": "hipBLASLt fp16 GEMM (torch.matmul), same shapes, no decode or epilogue", **out}
+
+
+def fp8_yardstick(c):
+    """hipBLASLt's FP8 GEMM (torch._scaled_mm: E4M3 operands, one scale per
+    tensor, bf16 out, no epilogue) on the same shapes, beside the row-wise FP8
+    path.  Reports the error instead if this torch build does not run it."""
+    import torch
+    out = {}
+    try:
+        for name, (m, n, k) in (("gemm_up", (TOKENS, MLP, HIDDEN)), ("gemm_down", (TOKENS, HIDDEN, MLP))):
+            a = torch.randn(m, k, device=c.x.device).to(torch.float8_e4m3fn)
+            w = torch.randn(n, k, device=c.x.device).to(torch.float8_e4m3fn)
+            one = torch.ones((), device=c.x.device, dtype=torch.float32)
+
+            def run(events, a=a, w=w, one=one):
+                mark = (lambda q: events[q].record(c.stream)) if events else (lambda q: None)
+                mark(0)
+                torch._scaled_mm(a, w.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+                mark(1)
+            _, st = timed_sequence(c, run, ["mm"])
+            flop = 2 * m * n * k
+            out[name] = {"shape": [m, n, k], "us": st["mm"],
+                         "TFLOPs": round(flop / (st["mm"] * 1e-6) / 1e12, 1)}
+            del a, w
+    except Exception as e:   # an fp8 GEMM this torch build cannot run: say so
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+    return {"what": "hipBLASLt FP8 GEMM (torch._scaled_mm, per-tensor scales, bf16 out, no epilogue)",
+            **out}
 
 
 def shapes_section(to_dev, ev, stream):
