@@ -833,7 +833,7 @@ using CfgPipe = Cfg<256, 256, 4, 2, 1>;    // 8 waves of 64x128 (v3)
 using CfgSmall = Cfg<128, 128, 2, 2, 2>;   // 4 waves of 64x64, 2 workgroups per CU (v1)
 using CfgTiny = Cfg<64, 64, 2, 2, 2>;      // 4 waves of 32x32 (v1), for few-tile problems
 
-// DiT-sized problems run v5 (K % 128 == 0, aligned rows) or v3 on 256x256
+// DiT-sized problems run v5 (K % 256 == 0, aligned buffers) or v3 on 256x256
 // tiles; small ones v1 on 128x128 tiles, two workgroups per CU, or on 64x64
 // tiles when 128x128 ones would leave more than half the compute units idle.
 // NVFP4_GEMM_KERNEL=tiny|small|pipe|v5 pins one (testing; v5 only where it
@@ -857,14 +857,15 @@ bool use_tiny(int64_t M, int64_t N) {
   return 2 * tiles128 < compute_units();
 }
 
-// v5 needs K % 128 == 0, 16-byte aligned code rows, 4-byte aligned scale
-// rows and code bytes below 4 GiB per operand (32-bit source offsets).
+// v5 needs K % 256 == 0 (an even number of stages; scale rows of a multiple
+// of 16 bytes), 16-byte aligned code and scale buffers and code bytes below
+// 4 GiB per operand (32-bit source offsets).
 bool v5_applies(int64_t M, int64_t N, int64_t K, uintptr_t code_bits, uintptr_t scale_bits) {
   if (const char* f = getenv("NVFP4_GEMM_KERNEL"))
     if (!strcmp(f, "pipe") || !strcmp(f, "small")) return false;
   const int64_t limit = (int64_t)1 << 32;
-  return K % kVBK == 0 && (code_bits & 15) == 0 && (scale_bits & 3) == 0 && M * (K / 2) < limit &&
-         N * (K / 2) < limit;
+  return K % (2 * kVBK) == 0 && (code_bits & 15) == 0 && (scale_bits & 15) == 0 &&
+         M * (K / 2) < limit && N * (K / 2) < limit;
 }
 
 struct SplitPlan {

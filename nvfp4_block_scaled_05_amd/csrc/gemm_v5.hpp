@@ -24,16 +24,18 @@ struct Out {
 namespace {
 
 // ---------------------------------------------------------------------------
-// v5: direct-to-LDS operands, both decoded in registers.  For K % 128 == 0.
+// v5: direct-to-LDS operands, both decoded in registers.  For K % 256 == 0
+// (an even number of 128-wide stages, and 16-byte aligned scale rows for the
+// paired scale loads).
 // Workgroup of 4 waves in 2x2 over a 256x256 tile, each wave 128x128 (4x4
 // MFMA tiles, 256 fp32 accumulators per lane).  K advances 128 per stage
 // (eight 16-K MFMA steps), triple-buffered in LDS; a stage holds per row 64
-// bytes of codes and 8 block-scale bytes of each operand (36 KB).
+// bytes of codes of each operand and room for 16 block-scale bytes (the
+// scales of two stages, loaded every other stage) (40 KB).
 //   * Codes and scales go from global memory straight into LDS (the gfx950
 //     buffer load with the LDS destination: one instruction fills 1 KB with
-//     16-byte pieces, or 256 B with 4-byte ones, lane L's at offset L times
-//     the size).  Inside a
-//     64-byte code row the 16-byte pieces are permuted by an XOR with
+//     16-byte pieces, lane L's at offset 16 L).  Inside a 64-byte code row
+//     the 16-byte pieces are permuted by an XOR with
 //     (row / 4) % 4, which makes the fragment reads (16 lanes, 16 consecutive
 //     rows, one logical piece) hit 16 different bank groups.
 //   * Same K permutation as v1-v3 at this width: lanes 0-31 of a wave take
@@ -41,7 +43,7 @@ namespace {
 //     takes code word s of each lane's 32 bytes, so A and W agree on k.
 //   * Each wave decodes its own 128 rows of A and 128 rows of W from the
 //     packed codes (no fp16 copy in LDS): LDS traffic is the codes only.
-//   * Three stage slots in LDS (108 KB): the loads of stage t+2 are issued
+//   * Three stage slots in LDS (120 KB): the loads of stage t+2 are issued
 //     during stage t, after its packed operands have all been read into
 //     registers, so no LDS read waits on a load in flight.
 //   * The decode of step s+1 is interleaved with the MFMAs of step s; the
@@ -57,17 +59,18 @@ constexpr int kVBM = 256, kVBN = 256, kVBK = 128, kVNT = 256;
 constexpr int kVWM = 128, kVWN = 128, kVTM = 4, kVTN = 4;
 constexpr int kVCodeRow = kVBK / 2;                 // 64 code bytes per row and stage
 constexpr int kVScaleRow = kVBK / 16;               // 8 scale bytes per row and stage
+constexpr int kVScalePair = 2 * kVScaleRow;         // a row's scales of two stages
 constexpr int kVA = 0;                              // A codes
 constexpr int kVW = kVA + kVBM * kVCodeRow;         // W codes
-constexpr int kVSA = kVW + kVBN * kVCodeRow;        // A scales
-constexpr int kVSW = kVSA + kVBM * kVScaleRow;      // W scales
-constexpr int kVStage = kVSW + kVBN * kVScaleRow;   // 36 KB
+constexpr int kVSA = kVW + kVBN * kVCodeRow;        // A scales, two stages per row
+constexpr int kVSW = kVSA + kVBM * kVScalePair;     // W scales, two stages per row
+constexpr int kVStage = kVSW + kVBN * kVScalePair;  // 40 KB
 
 // This lane's source offsets (bytes from the start of the operand's codes /
 // scales; rows * K / 2 < 2^32 is checked on the host).
 struct V5Src {
   uint32_t ac[4], wc[4];     // code chunks of 16 rows
-  uint32_t as[2], ws[2];     // scale chunks of 32 rows
+  uint32_t as, ws;           // start of the scale row this lane loads (row 64 * wave + lane)
 };
 
 __device__ __forceinline__ void v5_setup(int64_t M, int64_t N, int64_t K, int64_t m0, int64_t n0,
@@ -83,29 +86,35 @@ __device__ __forceinline__ void v5_setup(int64_t M, int64_t N, int64_t K, int64_
     d.ac[i] = (uint32_t)(ra * cpitch + piece * 16);
     d.wc[i] = (uint32_t)(rw * cpitch + piece * 16);
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 32 * (wave * 2 + i) + (lane >> 1);
+  {
+    const int row = 64 * wave + lane;
     const int64_t ra = m0 + row < M ? m0 + row : M - 1;
     const int64_t rw = n0 + row < N ? n0 + row : N - 1;
-    d.as[i] = (uint32_t)(ra * spitch + (lane & 1) * 4);
-    d.ws[i] = (uint32_t)(rw * spitch + (lane & 1) * 4);
+    d.as = (uint32_t)(ra * spitch);
+    d.ws = (uint32_t)(rw * spitch);
   }
 }
 
-// The global->LDS loads of one stage into `stage`, in six parts of two
-// instructions each: parts 0-3 the code chunks i of A and W, parts 4-5 the
-// scale chunks.  Inside the K loop the parts are spread over the stage's MFMA
-// steps, one part per step: issuing a load occupies the wave while the
-// compute unit's address unit takes its 64 addresses, and twelve of them in a
-// row (four waves at once) leave the matrix pipe idle for hundreds of clocks.
+// The global->LDS loads of one stage into `stage`: parts 0-3 the code chunks
+// i of A and W (two instructions each), part 4 the block scales.  Scales go in
+// pairs of stages: one 16-byte load per row brings a row's scales of stages
+// `pair` and `pair` + 1 (8 bytes each), so only every other stage loads them
+// (and an item's first stage, whatever its parity: the pair that holds it).
+// A stage of odd index then reads its scales from the slot of the stage
+// before it.  Inside the K loop the parts are spread over the stage's MFMA
+// steps: issuing a load occupies the wave while the compute unit's address
+// unit takes its 64 addresses, and all of a stage's loads in a row (four
+// waves at once) leave the matrix pipe idle for hundreds of clocks; the scale
+// loads, two of the old eight per wave and stage, cost as much to issue as
+// code loads that carry four times the bytes.
 struct V5Refill {
   const uint8_t* ac;
   const uint8_t* as;
   const uint8_t* wc;
   const uint8_t* ws;
   const V5Src* src;
-  int kt;
+  int kt;          // the stage's K index (codes)
+  int pair;        // the first stage of the scale pair to load, or -1: none
   uint8_t* stage;
 };
 
@@ -117,22 +126,29 @@ __device__ __forceinline__ void v5_issue_part(const V5Refill& r) {
     buffer_load_lds<16>(r.ac, r.src->ac[P], r.kt * kVCodeRow, r.stage + kVA + c * 1024);
     buffer_load_lds<16>(r.wc, r.src->wc[P], r.kt * kVCodeRow, r.stage + kVW + c * 1024);
   } else {
-    const int i = P - 4, c = wave * 2 + i;
-    buffer_load_lds<4>(r.as, r.src->as[i], r.kt * kVScaleRow, r.stage + kVSA + c * 256);
-    buffer_load_lds<4>(r.ws, r.src->ws[i], r.kt * kVScaleRow, r.stage + kVSW + c * 256);
+    // rows 64 * wave + lane, 16 bytes each: 1 KB per wave and operand
+    buffer_load_lds<16>(r.as, r.src->as, r.pair * kVScaleRow, r.stage + kVSA + wave * 1024);
+    buffer_load_lds<16>(r.ws, r.src->ws, r.pair * kVScaleRow, r.stage + kVSW + wave * 1024);
   }
 }
 
+// A whole stage at once (the first stages of an item): the scales first, so a
+// wait that lets the codes of the stage after stay in flight has them.
 __device__ __forceinline__ void v5_issue(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
                                          const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
-                                         const V5Src& d, int kt, uint8_t* stage) {
-  const V5Refill r{ac, as, wc, ws, &d, kt, stage};
+                                         const V5Src& d, int kt, int pair, uint8_t* stage) {
+  const V5Refill r{ac, as, wc, ws, &d, kt, pair, stage};
+  if (pair >= 0) v5_issue_part<4>(r);
   v5_issue_part<0>(r);
   v5_issue_part<1>(r);
   v5_issue_part<2>(r);
   v5_issue_part<3>(r);
-  v5_issue_part<4>(r);
-  v5_issue_part<5>(r);
+}
+
+// The scale pair an item's stage t (K index g = kb + t) loads: its own pair at
+// an even g, the pair holding it at the item's first stage, none otherwise.
+__device__ __forceinline__ int v5_pair(int g, int t) {
+  return (g & 1) == 0 ? g : t == 0 ? g - 1 : -1;
 }
 
 // One lane's packed operands for a stage: tiles 0-3 are A (i), 4-7 are W (j).
@@ -145,8 +161,10 @@ struct V5Ops {
   f16x8 v[8];
 };
 
-__device__ __forceinline__ void v5_read(const uint8_t* stage, int a_row, int w_row, int h, int x,
-                                        V5Packed& p, uint32_t (&sc)[8]) {
+// `scl`: the scales of this stage -- its own slot's pair area, or the
+// previous stage's, plus 8 bytes for the second stage of a pair.
+__device__ __forceinline__ void v5_read(const uint8_t* stage, const uint8_t* scl, int a_row,
+                                        int w_row, int h, int x, V5Packed& p, uint32_t (&sc)[8]) {
   const int p0 = ((2 * h) ^ x) << 4, p1 = ((2 * h + 1) ^ x) << 4;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -154,7 +172,7 @@ __device__ __forceinline__ void v5_read(const uint8_t* stage, int a_row, int w_r
     const uint8_t* cr = stage + (t < 4 ? kVA : kVW) + row * kVCodeRow;
     p.lo[t] = *reinterpret_cast<const u32x4*>(cr + p0);
     p.hi[t] = *reinterpret_cast<const u32x4*>(cr + p1);
-    sc[t] = *reinterpret_cast<const uint32_t*>(stage + (t < 4 ? kVSA : kVSW) + row * kVScaleRow + h * 4);
+    sc[t] = *reinterpret_cast<const uint32_t*>(scl + (t < 4 ? kVSA : kVSW) + row * kVScalePair + h * 4);
   }
 }
 
@@ -202,26 +220,28 @@ __device__ __forceinline__ void v5_mfma(const V5Ops& o, f32x16 (&acc)[kVTM][kVTN
 }
 
 // MFMAs of step S-1 (in `cur`) interleaved with the decode of step S (into
-// `nxt`); with LOAD, also part S - 1 of the refill, one load after the 8th
-// and one after the 16th MFMA.
+// `nxt`); with LOAD, steps 1-4 also issue code part S - 1 of the refill, one
+// load after the 8th and one after the 16th MFMA.
 template <int S, bool LOAD>
 __device__ __forceinline__ void v5_step(const V5Packed& p, const V5Ops& cur, V5Ops& nxt,
                                         f32x16 (&acc)[kVTM][kVTN], const V5Refill& r) {
+  constexpr bool L = LOAD && S <= 4;
   v5_decode<S>(p, nxt);
   v5_mfma(cur, acc);
-  if (LOAD) v5_issue_part<S - 1>(r);
+  if constexpr (L) v5_issue_part<S - 1>(r);
 #pragma unroll
   for (int m = 0; m < kVTM * kVTN; ++m) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU (decode)
-    if (LOAD && m % 8 == 7) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (load)
+    if (L && m % 8 == 7) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (load)
   }
 }
 
 // Steps of a stage whose step-0 operands are in `y` (`x` free): the MFMAs of
 // steps 0-5 and the decode of steps 1-7.  Leaves step 6's operands in `y`,
 // step 7's in `c`, and `x` free: those two steps run after the next barrier.
-// With LOAD the refill `r` is issued along the way, one part per step.
+// With LOAD the refill's code loads `r` are issued along the way, one part
+// per step.
 template <bool LOAD>
 __device__ __forceinline__ void v5_body(const V5Packed& p, V5Ops& x, V5Ops& y, V5Ops& c,
                                         f32x16 (&acc)[kVTM][kVTN], const V5Refill& r) {
@@ -233,18 +253,18 @@ __device__ __forceinline__ void v5_body(const V5Packed& p, V5Ops& x, V5Ops& y, V
   v5_decode<6>(p, y);                      // MFMAs of step 5 with two decodes
   v5_decode<7>(p, c);
   v5_mfma(x, acc);
-  if (LOAD) v5_issue_part<5>(r);
 #pragma unroll
   for (int m = 0; m < kVTM * kVTN; ++m) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU (decode)
-    if (LOAD && m % 8 == 7) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (load)
   }
 }
 
 // Stage data in LDS: this wave's loads for it have landed (vmcnt; with
-// `next_in_flight` the 12 loads issued since -- the following stage's -- may
-// still be outstanding; they complete in order), then the workgroup barrier
+// `next_in_flight` the 8 code loads of the following stage, its last loads,
+// may still be outstanding -- its scales went out before them; loads complete
+// in order, and any later memory instruction only makes the wait stricter),
+// then the workgroup barrier
 // makes every wave's loads visible and ends every read of the slot about to
 // be refilled.
 // (__syncthreads() would add a release fence, which waits for every load in
@@ -252,7 +272,7 @@ __device__ __forceinline__ void v5_body(const V5Packed& p, V5Ops& x, V5Ops& y, V
 // clobber keeps the compiler from moving memory accesses across it.)
 __device__ __forceinline__ void v5_barrier(bool next_in_flight) {
   if (next_in_flight)
-    __builtin_amdgcn_s_waitcnt(0x007C);   // vmcnt(12) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0078);   // vmcnt(8) lgkmcnt(0)
   else
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
   asm volatile("s_barrier" ::: "memory");
@@ -275,13 +295,14 @@ __device__ __forceinline__ void v5_barrier(bool next_in_flight) {
 template <bool REFILL>
 __device__ __forceinline__ void v5_stage(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
                                          const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
-                                         const V5Src& src, const uint8_t* cur, uint8_t* refill,
-                                         bool next_in_flight, int k_refill, int a_row, int w_row,
-                                         int h, int x_sw, V5Packed& p, V5Ops& x, V5Ops& s6,
-                                         V5Ops& c, f32x16 (&acc)[kVTM][kVTN]) {
+                                         const V5Src& src, const uint8_t* cur, const uint8_t* scl,
+                                         uint8_t* refill, bool next_in_flight, int k_refill,
+                                         int pair_refill, int a_row, int w_row, int h, int x_sw,
+                                         V5Packed& p, V5Ops& x, V5Ops& s6, V5Ops& c,
+                                         f32x16 (&acc)[kVTM][kVTN]) {
   v5_barrier(next_in_flight);
   uint32_t sc[8];
-  v5_read(cur, a_row, w_row, h, x_sw, p, sc);
+  v5_read(cur, scl, a_row, w_row, h, x_sw, p, sc);
   v5_mfma(s6, acc);                        // previous stage, step 6
 #pragma unroll
   for (int m = 0; m < 12; ++m) {
@@ -290,6 +311,10 @@ __device__ __forceinline__ void v5_stage(const uint8_t* __restrict__ ac, const u
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   __builtin_amdgcn_sched_barrier(0);
+  const V5Refill r{ac, as, wc, ws, &src, k_refill, pair_refill, refill};
+  // the refill's scale pair, if it loads one, first: the next stage's wait
+  // lets only its code loads stay in flight
+  if (REFILL && pair_refill >= 0) v5_issue_part<4>(r);
   v5_scales(sc, p);
   v5_decode<0>(p, s6);
   v5_mfma(c, acc);                         // previous stage, step 7
@@ -299,7 +324,6 @@ __device__ __forceinline__ void v5_stage(const uint8_t* __restrict__ ac, const u
     __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU (scales, decode, addresses)
   }
   __builtin_amdgcn_sched_barrier(0);
-  const V5Refill r{ac, as, wc, ws, &src, k_refill, refill};
   v5_body<REFILL>(p, x, s6, c, acc, r);
 }
 
@@ -530,6 +554,12 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
   static_assert(4 * 16384 <= 2 * kVStage, "the bf16 epilogue's staging leaves slot 2 free");
   __shared__ __attribute__((aligned(16))) float col_bias[kVBN];
 #define V5_SLOT(t) (lds + (((t) + 2) % 3) * kVStage)
+  // the scales of the item's stage t (K index kb + t): in the pair its own
+  // slot holds, or -- at an odd K index past the item's first stage -- in the
+  // second half of the pair the stage before it loaded
+#define V5_SCL(t)                                                                       \
+  ((((it.kb + (t)) & 1) && (t) > 0) ? V5_SLOT((t) - 1) + kVScaleRow                    \
+                                    : V5_SLOT(t) + ((it.kb + (t)) & 1) * kVScaleRow)
   const int64_t tiles_m = (M + kVBM - 1) / kVBM, tiles_n = (N + kVBN - 1) / kVBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -542,7 +572,7 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
   V5Item it = v5_item(b, tiles_m, tiles_n, sk, nk);
   V5Src src;
   v5_setup(M, N, K, it.m0, it.n0, src);
-  v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb, V5_SLOT(0));
+  v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb, v5_pair(it.kb, 0), V5_SLOT(0));
   u16x2 amax = {0, 0};
   for (;;) {
     {
@@ -560,12 +590,16 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
     const int ns = it.ke - it.kb;
     V5Packed p;
     V5Ops oa, ob, oc;
-    if (ns > 1) v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb + 1, V5_SLOT(1));
+    if (ns > 1)
+      v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb + 1, v5_pair(it.kb + 1, 1),
+               V5_SLOT(1));
     v5_barrier(ns > 1);
     {
       uint32_t sc[8];
-      v5_read(V5_SLOT(0), a_row, w_row, h, x, p, sc);
-      if (ns > 2) v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb + 2, V5_SLOT(2));
+      v5_read(V5_SLOT(0), V5_SCL(0), a_row, w_row, h, x, p, sc);
+      if (ns > 2)
+        v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb + 2, v5_pair(it.kb + 2, 2),
+                 V5_SLOT(2));
       v5_scales(sc, p);
     }
     v5_decode<0>(p, oa);
@@ -573,11 +607,12 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
     // every stage leaves its step 6 in oa and step 7 in oc, as this one
     int t = 1;
     for (; t + 2 < ns; ++t)                  // the stage two ahead is loaded
-      v5_stage<true>(a_codes, a_scales, w_codes, w_scales, src, V5_SLOT(t), V5_SLOT(t + 2), true,
-                     it.kb + t + 2, a_row, w_row, h, x, p, ob, oa, oc, acc);
+      v5_stage<true>(a_codes, a_scales, w_codes, w_scales, src, V5_SLOT(t), V5_SCL(t),
+                     V5_SLOT(t + 2), true, it.kb + t + 2, v5_pair(it.kb + t + 2, t + 2), a_row,
+                     w_row, h, x, p, ob, oa, oc, acc);
     for (; t < ns; ++t)                      // the last two: nothing more to load
-      v5_stage<false>(a_codes, a_scales, w_codes, w_scales, src, V5_SLOT(t), nullptr, t + 1 < ns,
-                      0, a_row, w_row, h, x, p, ob, oa, oc, acc);
+      v5_stage<false>(a_codes, a_scales, w_codes, w_scales, src, V5_SLOT(t), V5_SCL(t), nullptr,
+                      t + 1 < ns, 0, -1, a_row, w_row, h, x, p, ob, oa, oc, acc);
     v5_mfma(oa, acc);
     v5_mfma(oc, acc);
 
@@ -603,7 +638,7 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
       b = nb;
       it = v5_item(b, tiles_m, tiles_n, sk, nk);
       v5_setup(M, N, K, it.m0, it.n0, src);
-      v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb, V5_SLOT(0));
+      v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb, v5_pair(it.kb, 0), V5_SLOT(0));
       continue;
     }
     __syncthreads();   // every wave is done with the stage buffers
@@ -611,7 +646,7 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
       b = nb;
       it = v5_item(b, tiles_m, tiles_n, sk, nk);
       v5_setup(M, N, K, it.m0, it.n0, src);
-      v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb, V5_SLOT(0));
+      v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb, v5_pair(it.kb, 0), V5_SLOT(0));
     }
     float* st = reinterpret_cast<float*>(lds + wave * 16384);
     if (kQuant)   // bf16 staging after the four fp32 areas: 32 rows of 136 halves per wave
@@ -626,6 +661,7 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
     __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
   }
+#undef V5_SCL
 #undef V5_SLOT
   if (!kQuant && out.y_amax) {   // one atomic per workgroup
     __shared__ uint32_t wave_amax[kVNT / 64];
