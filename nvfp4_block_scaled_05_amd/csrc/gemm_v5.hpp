@@ -287,11 +287,12 @@ __device__ __forceinline__ void v5_barrier(bool next_in_flight) {
 // and `x` from step to step and leaves this stage's step 6 in `s6`, step 7 in
 // `c` and `x` free: the same roles the next stage expects, so the operand
 // sets are never copied.
-// `next_in_flight`: the following stage's loads are outstanding.  REFILL:
-// this stage issues the loads of stage t + 2 into `refill`, spread over its
-// steps 1-6 (after every LDS read of the stage, so no read waits on them);
-// compile-time, so the loads sit in the same basic blocks as the MFMAs they
-// are interleaved with.
+// `scl`: where this stage's scales are (see v5_read).  `next_in_flight`: the
+// following stage's loads are outstanding.  REFILL: this stage issues the
+// loads of stage t + 2 into `refill` (its scale pair `pair_refill`, if any,
+// then its codes over steps 1-4), after every LDS read of the stage, so no
+// read waits on them; compile-time, so the code loads sit in the same basic
+// blocks as the MFMAs they are interleaved with.
 template <bool REFILL>
 __device__ __forceinline__ void v5_stage(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
                                          const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
