@@ -398,6 +398,14 @@ def test_gemm_kernels_and_k_split(monkeypatch, M, N, K, kernel, split):
     assert_gemm_close(y, ref, f"{kernel}/{split} {M}x{N}x{K}")
 
 
+def test_gemm_large_odd_stage_count_default_kernel():
+    # a problem the 256x256 kernels take (M*N above 8.4M) whose K is an odd
+    # number of 128-wide stages: the paired scale loads of v5 need K % 256
+    # == 0, so the default choice runs v3 here; the result is the same GEMM
+    y, ref = _gemm_case(1024, 8448, 1152, seed=4242, bias=True, epilogue="gelu")
+    assert_gemm_close(y, ref, "1024x8448x1152 gelu")
+
+
 _V5_SHAPES = [(300, 520, 1280), (257, 300, 1024), (64, 33, 3072), (513, 256, 256), (256, 256, 512),
               (600, 700, 768)]
 
