@@ -413,8 +413,8 @@ __device__ __forceinline__ void dma_stage(const uint8_t* __restrict__ a, const u
 template <int EPI>
 __device__ __forceinline__ void fp8_slice_out(const float* st, const float* rs, f32x4 cs, f32x4 bv,
                                               int64_t row0, int64_t col, int64_t M, int64_t N,
-                                              bool vec, uint16_t* __restrict__ y) {
-  const int lane = threadIdx.x & 63, c = lane & 31;
+                                              bool vec, uint16_t* __restrict__ y, int lane) {
+  const int c = lane & 31;
   // four rows' reads first, then their 16 values (GELU one step across all
   // 16), then the stores: one LDS wait per 16 values and independent chains
   for (int it0 = 0; it0 < 16; it0 += 4) {
@@ -447,118 +447,173 @@ __device__ __forceinline__ void fp8_slice_out(const float* st, const float* rs, 
   }
 }
 
+// Work item b of a launch: a whole tile, or one K range of a tail tile
+// (split_coords_of on item b), with its first and last stage.
+struct DmaItem {
+  int64_t m0, n0, tail;
+  int split, kb, ke;
+};
+
+__device__ __forceinline__ DmaItem dma_item(int64_t b, int64_t tiles_m, int64_t tiles_n,
+                                            const SplitK& sk, int nk) {
+  DmaItem it;
+  int64_t tm, tn;
+  split_coords_of(b, tiles_m, tiles_n, sk, tm, tn, it.tail, it.split);
+  it.m0 = tm * kDBM;
+  it.n0 = tn * kDBN;
+  // the stage range is uniform; readfirstlane keeps it in scalar registers
+  // (the loads take their K offset as a scalar operand)
+  it.kb = __builtin_amdgcn_readfirstlane(it.split < 0 ? 0 : (int)((int64_t)it.split * nk / sk.ways));
+  it.ke = __builtin_amdgcn_readfirstlane(it.split < 0 ? nk : (int)((int64_t)(it.split + 1) * nk / sk.ways));
+  return it;
+}
+
+// Persistent: workgroup b takes work items b, b + gridDim.x, ... below
+// `items` (the grid is a multiple of the 8 XCDs, so every item of a
+// workgroup maps to its XCD's range of the tile order, as a one-item launch
+// would).  The epilogue stages the accumulators in buffer 1 only, so the next
+// item's first stage is loaded into buffer 0 while this item's epilogue runs.
 __global__ __launch_bounds__(kDNT, 1) void gemm_fp8_dma_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ da, const uint8_t* __restrict__ w,
     const float* __restrict__ dw, const uint16_t* __restrict__ bias, int64_t M, int64_t N,
-    int64_t K, int epi, uint16_t* __restrict__ y, SplitK sk) {
+    int64_t K, int epi, uint16_t* __restrict__ y, SplitK sk, int64_t items) {
   // two separately declared buffers, so that reads of one are seen not to
   // alias DMA writes into the other
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kDStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kDStage];
   __shared__ float row_scale[kDBM];
   __shared__ __attribute__((aligned(16))) float col_scale[kDBN], col_bias[kDBN];
+  static_assert(4 * 16384 <= kDStage, "the epilogue's staging fits in one buffer");
   const int64_t tiles_m = (M + kDBM - 1) / kDBM, tiles_n = (N + kDBN - 1) / kDBN;
-  int64_t tm, tn, tail;
-  int split;
-  split_coords(tiles_m, tiles_n, sk, tm, tn, tail, split);
-  const int64_t m0 = tm * kDBM, n0 = tn * kDBN;
-  {
-    const int64_t r = m0 + threadIdx.x, c = n0 + threadIdx.x;
-    row_scale[threadIdx.x] = r < M ? da[r] : 0.0f;
-    col_scale[threadIdx.x] = c < N ? dw[c] : 0.0f;
-    col_bias[threadIdx.x] = (bias && c < N) ? bf16_bits_to_f32(bias[c]) : 0.0f;
-  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, h = lane >> 5, sw = (r >> 1) & 7;
   const int a_off = (wm * kDWM + r) * kDBK, b_off = (wn * kDWN + r) * kDBK;
-
-  DmaPtrs ptr;
-  dma_setup(M, N, K, m0, n0, ptr);
-  f32x16 acc[kDTM][kDTN];
-#pragma unroll
-  for (int i = 0; i < kDTM; ++i)
-#pragma unroll
-    for (int j = 0; j < kDTN; ++j) acc[i][j] = f32x16{};
-
-  // stages [kb, ke) of 128 K: all of them, or this split's share
   const int nk = (int)(K / kDBK);
-  const int kb = split < 0 ? 0 : (int)((int64_t)split * nk / sk.ways);
-  const int ke = split < 0 ? nk : (int)((int64_t)(split + 1) * nk / sk.ways);
-  const int ns = ke - kb;
-  DmaFrags f0, f1;
-  dma_issue(a, w, ptr, (int64_t)kb * kDBK, lds0);
-  dma_barrier();
-  if (ns > 1) dma_issue(a, w, ptr, (int64_t)(kb + 1) * kDBK, lds1);
-  dma_frags<0>(lds0, a_off, b_off, h, sw, f0);
-  dma_frags<1>(lds0, a_off, b_off, h, sw, f1);
-  dma_mfma(f0, acc);
-  // stage kb + t reads buffer t % 2 and refills the other with stage kb + t + 1;
-  // whole pairs of stages, then at most one more
-  // whole pairs of stages, then at most one more.  Both stages of a pair
-  // load: the second stage of the last pair, with no stage left to load,
-  // loads its own stage again into the buffer nothing reads any more (a
-  // branch around its loads would take them out of the MFMAs' basic block);
-  // those loads are waited for before the epilogue or the partial stores.
-  int t = 1;
-  for (; t + 1 < ns; t += 2) {
-    dma_stage<true>(a, w, lds1, lds0, ptr, (int64_t)(kb + t + 1) * kDBK, a_off, b_off, h, sw, f0, f1,
-                    acc);
-    const int k2 = t + 2 < ns ? kb + t + 2 : kb + t + 1;
-    dma_stage<true>(a, w, lds0, lds1, ptr, (int64_t)k2 * kDBK, a_off, b_off, h, sw, f0, f1, acc);
-  }
-  if (t < ns) dma_stage<false>(a, w, lds1, lds0, ptr, 0, a_off, b_off, h, sw, f0, f1, acc);
-  dma_mfma(f1, acc);
-  __builtin_amdgcn_s_waitcnt(0);           // every load into LDS has landed
 
-  if (split >= 0) {
-    // a tail split: fp32 partial sums into its slice in accumulator order --
-    // float4 number (((wave * 4 + i) * 4 + j) * 64 + lane) * 4 + g holds
-    // acc[i][j][4g .. 4g+3], so each wave writes 4 KB contiguous per tile
-    f32x4* slice = reinterpret_cast<f32x4*>(sk.part + (tail * sk.ways + split) * (int64_t)(kDBM * kDBN));
+  int64_t b = blockIdx.x;
+  DmaItem it = dma_item(b, tiles_m, tiles_n, sk, nk);
+  DmaPtrs ptr;
+  dma_setup(M, N, K, it.m0, it.n0, ptr);
+  dma_issue(a, w, ptr, (int64_t)it.kb * kDBK, lds0);
+  for (;;) {
+    {
+      const int64_t rr = it.m0 + threadIdx.x, c = it.n0 + threadIdx.x;
+      row_scale[threadIdx.x] = rr < M ? da[rr] : 0.0f;
+      col_scale[threadIdx.x] = c < N ? dw[c] : 0.0f;
+      col_bias[threadIdx.x] = (bias && c < N) ? bf16_bits_to_f32(bias[c]) : 0.0f;
+    }
+    f32x16 acc[kDTM][kDTN];
 #pragma unroll
     for (int i = 0; i < kDTM; ++i)
 #pragma unroll
+      for (int j = 0; j < kDTN; ++j) acc[i][j] = f32x16{};
+
+    // stages [kb, ke) of 128 K: all of them, or this split's share; the
+    // first one is already issued
+    const int kb = it.kb, ns = it.ke - it.kb;
+    DmaFrags f0, f1;
+    dma_barrier();
+    if (ns > 1) dma_issue(a, w, ptr, (int64_t)(kb + 1) * kDBK, lds1);
+    dma_frags<0>(lds0, a_off, b_off, h, sw, f0);
+    dma_frags<1>(lds0, a_off, b_off, h, sw, f1);
+    dma_mfma(f0, acc);
+    // stage kb + t reads buffer t % 2 and refills the other with stage
+    // kb + t + 1; whole pairs of stages, then at most one more.  Both stages
+    // of a pair load: the second stage of the last pair, with no stage left
+    // to load, loads its own stage again into the buffer nothing reads any
+    // more (a branch around its loads would take them out of the MFMAs'
+    // basic block); those loads are waited for before the epilogue or the
+    // partial stores.
+    int t = 1;
+    for (; t + 1 < ns; t += 2) {
+      dma_stage<true>(a, w, lds1, lds0, ptr, (int64_t)(kb + t + 1) * kDBK, a_off, b_off, h, sw, f0,
+                      f1, acc);
+      const int k2 = t + 2 < ns ? kb + t + 2 : kb + t + 1;
+      dma_stage<true>(a, w, lds0, lds1, ptr, (int64_t)k2 * kDBK, a_off, b_off, h, sw, f0, f1, acc);
+    }
+    if (t < ns) dma_stage<false>(a, w, lds1, lds0, ptr, 0, a_off, b_off, h, sw, f0, f1, acc);
+    dma_mfma(f1, acc);
+    __builtin_amdgcn_s_waitcnt(0);           // every load into LDS has landed
+
+    const DmaItem cur = it;
+    const int64_t nb = b + gridDim.x;
+    const bool has_next = nb < items;
+    if (cur.split >= 0) {
+      // a tail split: fp32 partial sums into its slice in accumulator order --
+      // float4 number (((wave * 4 + i) * 4 + j) * 64 + lane) * 4 + g holds
+      // acc[i][j][4g .. 4g+3], so each wave writes 4 KB contiguous per tile
+      f32x4* slice =
+          reinterpret_cast<f32x4*>(sk.part + (cur.tail * sk.ways + cur.split) * (int64_t)(kDBM * kDBN));
+#pragma unroll
+      for (int i = 0; i < kDTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kDTN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            slice[(((wave * kDTM + i) * kDTN + j) * 64 + lane) * 4 + g] =
+                f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+      if (!has_next) break;
+      asm volatile("s_barrier" ::: "memory");   // every wave is done reading this item's buffers
+      b = nb;
+      it = dma_item(b, tiles_m, tiles_n, sk, nk);
+      dma_setup(M, N, K, it.m0, it.n0, ptr);
+      dma_issue(a, w, ptr, (int64_t)it.kb * kDBK, lds0);
+      continue;
+    }
+    __syncthreads();   // every wave is done with the stage buffers
+    if (has_next) {    // the next item's first stage, into buffer 0, under the epilogue
+      b = nb;
+      it = dma_item(b, tiles_m, tiles_n, sk, nk);
+      dma_setup(M, N, K, it.m0, it.n0, ptr);
+      dma_issue(a, w, ptr, (int64_t)it.kb * kDBK, lds0);
+    }
+
+    // epilogue: (acc * (dA[m] * dW[n]) + bias) -> GELU -> bf16, the
+    // operations of gemm_fp8_kernel's epilogue in the same order.  Fully
+    // unrolled over 256 accumulators per lane this would be more code than
+    // the instruction cache holds, so each wave moves 32 rows of its
+    // accumulators at a time into its own 16 KB of buffer 1 (fp32, 16-byte
+    // chunks of a 512-byte row permuted by XOR with the row) and a short loop
+    // takes them back 4 columns per lane.
+    // The lane index passes through an empty asm statement, so the staging
+    // addresses derived from it are computed here for every item instead of
+    // being hoisted out of the item loop, where they would hold registers
+    // through the main loop.
+    int le = lane;
+    asm volatile("" : "+v"(le));
+    const int re = le & 31, he = le >> 5;
+    float* st = reinterpret_cast<float*>(lds1 + wave * 16384);
+    const bool vec = cur.m0 + kDBM <= M && cur.n0 + kDBN <= N && N % 4 == 0 &&
+                     (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+    const int cq = wn * kDWN + re * 4;                      // this lane's 4 columns on read-back
+    const f32x4 cs = *reinterpret_cast<const f32x4*>(col_scale + cq);
+    const f32x4 bv = *reinterpret_cast<const f32x4*>(col_bias + cq);
+#pragma unroll
+    for (int i = 0; i < kDTM; ++i) {
+#pragma unroll
       for (int j = 0; j < kDTN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          slice[(((wave * kDTM + i) * kDTN + j) * 64 + lane) * 4 + g] =
+        for (int g = 0; g < 4; ++g) {
+          const int c = j * 8 + g * 2 + he;
+          *reinterpret_cast<f32x4*>(st + re * 128 + ((c ^ re) << 2)) =
               f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-    return;
-  }
-
-  // epilogue: (acc * (dA[m] * dW[n]) + bias) -> GELU -> bf16, the operations
-  // of gemm_fp8_kernel's epilogue in the same order.  Fully unrolled over 256
-  // accumulators per lane this would be more code than the instruction cache
-  // holds, so each wave moves 32 rows of its accumulators at a time into its
-  // own 16 KB of LDS (fp32, 16-byte chunks of a 512-byte row permuted by XOR
-  // with the row) and a short loop takes them back 4 columns per lane.
-  __syncthreads();   // every wave is done with the stage buffers
-  float* st = reinterpret_cast<float*>(lds0 + wave * 16384);
-  const bool vec = m0 + kDBM <= M && n0 + kDBN <= N && N % 4 == 0 &&
-                   (reinterpret_cast<uintptr_t>(y) & 7) == 0;
-  const int cq = wn * kDWN + (lane & 31) * 4;             // this lane's 4 columns on read-back
-  const f32x4 cs = *reinterpret_cast<const f32x4*>(col_scale + cq);
-  const f32x4 bv = *reinterpret_cast<const f32x4*>(col_bias + cq);
-#pragma unroll
-  for (int i = 0; i < kDTM; ++i) {
-#pragma unroll
-    for (int j = 0; j < kDTN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = j * 8 + g * 2 + h;
-        *reinterpret_cast<f32x4*>(st + r * 128 + ((c ^ r) << 2)) =
-            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-      }
-    __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-    const int rl0 = wm * kDWM + i * 32;
-    if (epi == 1)
-      fp8_slice_out<1>(st, row_scale + rl0, cs, bv, m0 + rl0, n0 + cq, M, N, vec, y);
-    else
-      fp8_slice_out<0>(st, row_scale + rl0, cs, bv, m0 + rl0, n0 + cq, M, N, vec, y);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_wave_barrier();
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      const int rl0 = wm * kDWM + i * 32;
+      if (epi == 1)
+        fp8_slice_out<1>(st, row_scale + rl0, cs, bv, cur.m0 + rl0, cur.n0 + cq, M, N, vec, y, le);
+      else
+        fp8_slice_out<0>(st, row_scale + rl0, cs, bv, cur.m0 + rl0, cur.n0 + cq, M, N, vec, y, le);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (!has_next) break;
+    // every wave is done with the staging and the row and column arrays
+    // before the next item's second stage refills buffer 1 and its scales
+    // are written
+    asm volatile("s_barrier" ::: "memory");
   }
 }
 
@@ -705,11 +760,18 @@ hipError_t launch_gemm_fp8(const uint8_t* a_codes, const float* a_scales, const 
     const bool split = plan.ways > 1 && workspace && workspace_bytes >= plan.bytes;
     const SplitK sk = split ? SplitK{static_cast<float*>(workspace), plan.main_tiles, plan.ways}
                             : SplitK{nullptr, plan.tiles, 1};
-    const int64_t grid = split ? plan.main_tiles + plan.tail * plan.ways : plan.tiles;
+    const int64_t items = split ? plan.main_tiles + plan.tail * plan.ways : plan.tiles;
+    // persistent grid, one workgroup per compute unit, when there are more
+    // items than compute units and the units divide into whole XCD groups
+    // (NVFP4_GEMM_PERSISTENT=0: one item per workgroup)
+    const int cus = compute_units();
+    const char* pe = getenv("NVFP4_GEMM_PERSISTENT");
+    const bool persistent = items > cus && cus % kXcds == 0 && !(pe && strcmp(pe, "0") == 0);
+    const int64_t grid = persistent ? cus : items;
     const uint16_t* b16 = reinterpret_cast<const uint16_t*>(bias);
     uint16_t* y16 = reinterpret_cast<uint16_t*>(y);
     hipLaunchKernelGGL(gemm_fp8_dma_kernel, dim3((unsigned)grid), dim3(kDNT), 0, stream, a_codes,
-                       a_scales, w_codes, w_scales, b16, M, N, K, epilogue, y16, sk);
+                       a_scales, w_codes, w_scales, b16, M, N, K, epilogue, y16, sk, items);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || !split) return e;
     hipLaunchKernelGGL(fp8_split_reduce_kernel, dim3((unsigned)(plan.tail * kFp8ReduceWgs)),

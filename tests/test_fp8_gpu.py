@@ -8,7 +8,7 @@ import nvfp4_block_scaled_05_amd as nv
 from nvfp4_block_scaled_05_amd import inputs as W
 from oracle import (dequantize_fp8_rowwise, gemm_fp8_exact_rows, gemm_fp8_fp64,
                     quantize_fp8_rowwise)
-from tests.gpu_util import bits_of, rel_frobenius, to_dev, ulp_diff
+from tests.gpu_util import bits_of, rel_frobenius, stratified_rows, to_dev, ulp_diff
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,7 @@ def _close(y, ref, label):
 
 # K % 128 == 0 runs the direct-to-LDS kernel (1, 2, 3, 4, 9, 10 stages of 128,
 # ragged M and N); other K the register-staged one.  "reg" pins the latter.
+# These grids have fewer tiles than compute units: one tile per workgroup.
 GEMM_SHAPES = [(64, 64, 64), (130, 70, 48), (300, 257, 1088), (200, 300, 3088), (1, 129, 16),
                (513, 256, 512), (1, 1, 128), (256, 256, 256), (257, 513, 384),
                (300, 257, 1152), (70, 600, 1280)]
@@ -112,7 +113,10 @@ def test_fp8_gemm_mlp_up_sampled_rows():
     qx, rx = check_fp8_quantize(d["x"], "X")
     qw, rw = check_fp8_quantize(d["w_up"], "W_up")
     y = bits_of(nv.fp8_gemm(qx, qw, epilogue="gelu"))
-    rows = np.unique(np.concatenate([[0, 16895], np.random.default_rng(0).choice(16896, 40, replace=False)]))
+    # a row in every 256-row tile band (each row covers all 48 column tiles of
+    # its band, so every tile of the persistent grid is checked)
+    rows = np.unique(np.concatenate([stratified_rows(16896), [16895],
+                                     np.random.default_rng(0).choice(16896, 16, replace=False)]))
     ref, _ = gemm_fp8_exact_rows(rx, rw, rows, gelu=True)
     _close(y[rows], ref, "fp8 up sampled rows")
 
@@ -127,7 +131,7 @@ def test_fp8_gemm_mlp_down_sampled_rows():
     qw, rw = check_fp8_quantize(d["w_down"], "W_down")
     b_bits = W.random_matrix(78, (1, 3072), "normal", 0.1)[0]
     y = bits_of(nv.fp8_gemm(qh, qw, bias=to_dev(b_bits)))
-    rows = np.unique(np.concatenate([[0, 16895], rng.choice(16896, 24, replace=False)]))
+    rows = np.unique(np.concatenate([stratified_rows(16896), [16895], rng.choice(16896, 8, replace=False)]))
     ref, _ = gemm_fp8_exact_rows(rh, rw, rows, bias_bits=b_bits)
     _close(y[rows], ref, "fp8 down sampled rows")
 
@@ -152,3 +156,29 @@ def test_fp8_gemm_split_k(M, N, K, ways, monkeypatch):
         _close(y1, ref, f"fp8 split {ways} {M}x{N}x{K} {epi}")
         y0 = bits_of(nv.fp8_gemm(qa, qw, bias=to_dev(b_bits), epilogue=epi, workspace=None))
         _close(y0, ref, f"fp8 whole tiles {M}x{N}x{K} {epi}")
+
+
+@pytest.mark.parametrize("M,N,K", [(4352, 4096, 384), (4352, 4096, 2048)])
+def test_fp8_gemm_persistent_grid(M, N, K, monkeypatch):
+    # 272 tiles, more than the compute units: the persistent grid, each
+    # workgroup looping over tiles (and, at K = 2048, over the K ranges of the
+    # 16 split tail tiles), the next tile's first stage loaded under the
+    # epilogue.  K = 384 gives an odd number of stages.  The whole output
+    # against the oracle; then one item per workgroup and no split give the
+    # same bytes.
+    a_bits = W.random_matrix(M + 7 * K, (M, K), "t3")
+    w_bits = W.random_matrix(N + 7 * K, (N, K), "normal", 0.02)
+    b_bits = W.random_matrix(M + N + 9, (1, N), "normal", 0.1)[0]
+    qa, ra = check_fp8_quantize(a_bits, "A")
+    qw, rw = check_fp8_quantize(w_bits, "W")
+    ws = nv.fp8_gemm_workspace(M, N, K)
+    bias = to_dev(b_bits)
+    y = bits_of(nv.fp8_gemm(qa, qw, bias=bias, epilogue="gelu", workspace=ws))
+    ref, _ = gemm_fp8_fp64(ra, rw, bias_bits=b_bits, gelu=True)
+    _close(y, ref, f"fp8 persistent {M}x{N}x{K}")
+    monkeypatch.setenv("NVFP4_GEMM_PERSISTENT", "0")
+    y1 = bits_of(nv.fp8_gemm(qa, qw, bias=bias, epilogue="gelu", workspace=ws))
+    assert np.array_equal(y, y1), "persistent and one-item grids differ"
+    monkeypatch.delenv("NVFP4_GEMM_PERSISTENT")
+    y2 = bits_of(nv.fp8_gemm(qa, qw, bias=bias, epilogue="gelu", workspace=None))
+    _close(y2, ref, f"fp8 persistent, no split {M}x{N}x{K}")
