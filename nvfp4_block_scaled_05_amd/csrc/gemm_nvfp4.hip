@@ -986,15 +986,18 @@ hipError_t launch_v5(const uint8_t* a_codes, const uint8_t* a_scales, const floa
                           : SplitK{nullptr, plan.tiles, 1};
   const int64_t items = split ? plan.main_tiles + plan.tail * plan.ways : plan.tiles;
   const uint16_t* b16 = reinterpret_cast<const uint16_t*>(bias);
-  if (out.codes)   // NVFP4 output: whole tiles, one per workgroup
-    return launch_v5_quant(a_codes, a_scales, sa, w_codes, w_scales, sw, b16, M, N, K, epi, out,
-                           plan.tiles, stream);
   // persistent grid, one workgroup per compute unit, when there are more
   // items than compute units and the units divide into whole XCD groups
   // (NVFP4_GEMM_PERSISTENT=0: one item per workgroup)
   const int cus = compute_units();
   const char* pe = getenv("NVFP4_GEMM_PERSISTENT");
-  const bool persistent = items > cus && cus % kXcds == 0 && !(pe && strcmp(pe, "0") == 0);
+  const bool no_persist = pe && strcmp(pe, "0") == 0;
+  if (out.codes) {   // NVFP4 output: whole tiles
+    const bool persistent = plan.tiles > cus && cus % kXcds == 0 && !no_persist;
+    return launch_v5_quant(a_codes, a_scales, sa, w_codes, w_scales, sw, b16, M, N, K, epi, out,
+                           plan.tiles, persistent ? cus : plan.tiles, stream);
+  }
+  const bool persistent = items > cus && cus % kXcds == 0 && !no_persist;
   const int64_t grid = persistent ? cus : items;
   hipLaunchKernelGGL(gemm_nvfp4_v5_kernel<false>, dim3((unsigned)grid), dim3(kVNT), 0, stream, a_codes,
                      a_scales, sa, w_codes, w_scales, sw, b16, M, N, K, epi, out, sk, items);

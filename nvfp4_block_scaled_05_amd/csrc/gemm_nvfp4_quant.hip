@@ -9,9 +9,9 @@ namespace nvfp4 {
 hipError_t launch_v5_quant(const uint8_t* a_codes, const uint8_t* a_scales, const float* sa,
                            const uint8_t* w_codes, const uint8_t* w_scales, const float* sw,
                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, int epi,
-                           const Out& out, int64_t tiles, hipStream_t stream) {
+                           const Out& out, int64_t tiles, int64_t grid, hipStream_t stream) {
   const SplitK whole{nullptr, tiles, 1};
-  hipLaunchKernelGGL(gemm_nvfp4_v5_kernel<true>, dim3((unsigned)tiles), dim3(kVNT), 0, stream,
+  hipLaunchKernelGGL(gemm_nvfp4_v5_kernel<true>, dim3((unsigned)grid), dim3(kVNT), 0, stream,
                      a_codes, a_scales, sa, w_codes, w_scales, sw, bias, M, N, K, epi, out, whole,
                      tiles);
   return hipGetLastError();

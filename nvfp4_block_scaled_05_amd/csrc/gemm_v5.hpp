@@ -424,6 +424,12 @@ __device__ __forceinline__ u16x2 v5_epilogue(const f32x16 (&acc)[kVTM][kVTN], fl
 // staged in the wave's LDS, 32 rows x 128 columns at a time, and every lane
 // then quantizes whole 16-element blocks with the quantizer's own routine --
 // the bytes nvfp4_quantize writes for the bf16 output.  N % 16 == 0.
+// The bf16 rows (272-byte pitch) overlay the fp32 rows they come from
+// (512-byte pitch) in the same area: bf16 row R ends at byte 272 R + 272,
+// never past the start of fp32 row R + 1, so a row's bf16 values only
+// overwrite fp32 rows already read; the rows are read and written in
+// increasing order, and a compiler fence keeps each group's reads before its
+// writes (the hardware runs a wave's LDS accesses in order).
 template <int EPI>
 __device__ __forceinline__ void v5_slice_quant(const float* st, uint16_t* st16, float scale, f32x4 bv,
                                                int64_t row0, int64_t col_w, int64_t M, int64_t N,
@@ -438,6 +444,9 @@ __device__ __forceinline__ void v5_slice_quant(const float* st, uint16_t* st16, 
       const int rr = (it0 + u) * 2 + (lane >> 5);
       a4[u] = *reinterpret_cast<const f32x4*>(st + rr * 128 + ((c ^ rr) << 2));
     }
+    // the group's reads stay before its writes: a lane's bf16 row can
+    // overlay another lane's fp32 row of the same group
+    asm volatile("" ::: "memory");
     f32x4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -532,7 +541,7 @@ __device__ __forceinline__ V5Item v5_item(int64_t b, int64_t tiles_m, int64_t ti
 }
 
 // kQuant: NVFP4 output (out.codes, out.scales, out.tensor_scale) instead of
-// bf16 (out.y, out.y_amax); whole tiles only, one per workgroup.
+// bf16 (out.y, out.y_amax); whole tiles only.
 // Persistent: workgroup b takes work items b, b + gridDim.x, ... below
 // `items` (the grid is a multiple of the 8 XCDs, so every item of a
 // workgroup maps to its XCD's range of the tile order, as a one-item launch
@@ -550,9 +559,9 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
     SplitK sk, int64_t items) {
   // three stage slots: the loads of stage t + 2 are issued while stage t runs
   __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * kVStage];
-  static_assert(4 * 16384 + 4 * 32 * 136 * 2 + 4 * 512 <= 3 * kVStage,
-                "epilogue staging and encode-factor tables fit in the stage ring");
-  static_assert(4 * 16384 <= 2 * kVStage, "the bf16 epilogue's staging leaves slot 2 free");
+  static_assert(32 * 136 * 2 <= 16384, "a wave's bf16 rows fit in its fp32 staging area");
+  static_assert(4 * 16384 + 4 * 512 <= 2 * kVStage,
+                "the epilogue's staging and encode-factor tables leave slot 2 free");
   __shared__ __attribute__((aligned(16))) float col_bias[kVBN];
 #define V5_SLOT(t) (lds + (((t) + 2) % 3) * kVStage)
   // the scales of the item's stage t (K index kb + t): in the pair its own
@@ -650,10 +659,10 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
       v5_issue(a_codes, a_scales, w_codes, w_scales, src, it.kb, v5_pair(it.kb, 0), V5_SLOT(0));
     }
     float* st = reinterpret_cast<float*>(lds + wave * 16384);
-    if (kQuant)   // bf16 staging after the four fp32 areas: 32 rows of 136 halves per wave
+    if (kQuant)   // bf16 rows over the wave's fp32 area; encode factors after the four areas
       v5_epilogue_quant(acc, scale, col_bias, epi, M, N, cur.m0, cur.n0, out, st,
-                        reinterpret_cast<uint16_t*>(lds + 4 * 16384 + wave * 32 * 136 * 2),
-                        reinterpret_cast<float*>(lds + 4 * 16384 + 4 * 32 * 136 * 2 + wave * 512));
+                        reinterpret_cast<uint16_t*>(st),
+                        reinterpret_cast<float*>(lds + 4 * 16384 + wave * 512));
     else
       amax = max_u16x2(amax, v5_epilogue(acc, scale, col_bias, epi, M, N, cur.m0, cur.n0, out.y, st));
     if (!has_next) break;
@@ -681,11 +690,11 @@ __global__ __launch_bounds__(kVNT, 1) void gemm_nvfp4_v5_kernel(
 
 }  // namespace
 
-// gemm_nvfp4_v5_kernel<true> over `tiles` whole tiles, one per workgroup
-// (defined in gemm_nvfp4_quant.hip).
+// gemm_nvfp4_v5_kernel<true> over `tiles` whole tiles on `grid` workgroups
+// (tiles, or the persistent grid; defined in gemm_nvfp4_quant.hip).
 hipError_t launch_v5_quant(const uint8_t* a_codes, const uint8_t* a_scales, const float* sa,
                            const uint8_t* w_codes, const uint8_t* w_scales, const float* sw,
                            const uint16_t* bias, int64_t M, int64_t N, int64_t K, int epi,
-                           const Out& out, int64_t tiles, hipStream_t stream);
+                           const Out& out, int64_t tiles, int64_t grid, hipStream_t stream);
 
 }  // namespace nvfp4

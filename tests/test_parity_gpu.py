@@ -510,11 +510,14 @@ def torch_equal(u, v):
     return bool(torch.equal(u, v))
 
 
-@pytest.mark.parametrize("kernel", ["default", "pipe"])
+@pytest.mark.parametrize("kernel", ["default", "pipe", "one_item"])
 def test_gemm_quantized_mlp_up_full_size(monkeypatch, kernel):
     # H of the MLP at 2048^2 written straight in NVFP4 under a static amax
+    # (default: v5 on the persistent grid; one_item: v5, one tile per workgroup)
     import torch
-    if kernel != "default":
+    if kernel == "one_item":
+        monkeypatch.setenv("NVFP4_GEMM_PERSISTENT", "0")
+    elif kernel != "default":
         monkeypatch.setenv("NVFP4_GEMM_KERNEL", kernel)
     x_bits = _mlp()["x"]
     wu_bits, _ = _oracle_weight("w_up")
@@ -527,6 +530,19 @@ def test_gemm_quantized_mlp_up_full_size(monkeypatch, kernel):
     _sync()
     assert torch_equal(fused.codes, two.codes) and torch_equal(fused.scales, two.scales)
     assert torch_equal(fused.tensor_scale, two.tensor_scale)
+
+
+def test_gemm_quantized_persistent_ragged():
+    # 18 x 17 = 306 tiles of 256x256, more than the compute units: the
+    # persistent grid over tiles with ragged rows and columns, GELU and bias,
+    # against nvfp4_gemm followed by nvfp4_quantize
+    import torch
+    M, N, K = 4400, 4112, 512
+    for factor, epi, bias in ((1.0, "gelu", True), (0.25, "none", False)):
+        y, static, fused, two = _gemm_quantized_case(M, N, K, 4242, factor, epi, bias)
+        for u, v, what in ((fused.codes, two.codes, "codes"), (fused.scales, two.scales, "scales"),
+                           (fused.tensor_scale, two.tensor_scale, "tensor scale")):
+            assert torch_equal(u, v), f"persistent {M}x{N}x{K} amax*{factor}: {what}"
 
 
 def test_gemm_quantized_nonfinite_amax():
