@@ -218,6 +218,16 @@ __device__ __forceinline__ f16x8 decode8(uint32_t w, _Float16 s) {
 // that threadIdx.x >> 6 is uniform across a wave): LDS destinations of the
 // global->LDS loads, which go through M0, are then computed in scalar
 // registers instead of one v_readfirstlane per load.
+// The lane index through an empty asm statement.  A persistent kernel's
+// epilogue takes its lane-derived addresses from this, so they are computed
+// in the epilogue instead of being hoisted out of the item loop, where they
+// would hold registers through the main loop (and spill).
+__device__ __forceinline__ int opaque_lane() {
+  int l = (int)(threadIdx.x & 63);
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }

@@ -415,6 +415,7 @@ __device__ __forceinline__ void fp8_slice_out(const float* st, const float* rs, 
                                               int64_t row0, int64_t col, int64_t M, int64_t N,
                                               bool vec, uint16_t* __restrict__ y, int lane) {
   const int c = lane & 31;
+  asm volatile("" : "+v"(row0));   // row offsets computed here, not hoisted (see opaque_lane)
   // four rows' reads first, then their 16 values (GELU one step across all
   // 16), then the stores: one LDS wait per 16 values and independent chains
   for (int it0 = 0; it0 < 16; it0 += 4) {
@@ -576,13 +577,7 @@ __global__ __launch_bounds__(kDNT, 1) void gemm_fp8_dma_kernel(
     // accumulators at a time into its own 16 KB of buffer 1 (fp32, 16-byte
     // chunks of a 512-byte row permuted by XOR with the row) and a short loop
     // takes them back 4 columns per lane.
-    // The lane index passes through an empty asm statement, so the staging
-    // addresses derived from it are computed here for every item instead of
-    // being hoisted out of the item loop, where they would hold registers
-    // through the main loop.
-    int le = lane;
-    asm volatile("" : "+v"(le));
-    const int re = le & 31, he = le >> 5;
+    const int le = opaque_lane(), re = le & 31, he = le >> 5;
     float* st = reinterpret_cast<float*>(lds1 + wave * 16384);
     const bool vec = cur.m0 + kDBM <= M && cur.n0 + kDBN <= N && N % 4 == 0 &&
                      (reinterpret_cast<uintptr_t>(y) & 7) == 0;

@@ -341,7 +341,8 @@ template <int EPI>
 __device__ __forceinline__ u16x2 v5_slice_out(const float* st, float scale, f32x4 bv, int64_t row0,
                                               int64_t col, int64_t M, int64_t N, bool vec,
                                               uint16_t* __restrict__ y) {
-  const int lane = threadIdx.x & 63, c = lane & 31;
+  const int lane = opaque_lane(), c = lane & 31;
+  asm volatile("" : "+v"(row0));   // row offsets computed here, not hoisted (see opaque_lane)
   u16x2 amax = {0, 0};
   // four rows' reads first, then their 16 values, then the stores: one LDS
   // wait per 16 values and 16 independent chains for the scheduler to
@@ -388,7 +389,7 @@ __device__ __forceinline__ u16x2 v5_epilogue(const f32x16 (&acc)[kVTM][kVTN], fl
                                              const float* col_bias, int epi, int64_t M, int64_t N,
                                              int64_t m0, int64_t n0, uint16_t* __restrict__ y,
                                              float* st) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = opaque_lane(), wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, r = lane & 31, h = lane >> 5;
   const bool vec = m0 + kVBM <= M && n0 + kVBN <= N && N % 4 == 0 &&
                    (reinterpret_cast<uintptr_t>(y) & 7) == 0;
@@ -435,7 +436,8 @@ __device__ __forceinline__ void v5_slice_quant(const float* st, uint16_t* st16, 
                                                int64_t row0, int64_t col_w, int64_t M, int64_t N,
                                                bool degenerate, float s_enc, const float* e_of,
                                                const Out& out) {
-  const int lane = threadIdx.x & 63, c = lane & 31;
+  const int lane = opaque_lane(), c = lane & 31;
+  asm volatile("" : "+v"(row0));   // row offsets computed here, not hoisted (see opaque_lane)
   // four rows' reads first, then their 16 values (as in v5_slice_out)
   for (int it0 = 0; it0 < 16; it0 += 4) {
     f32x4 a4[4];
@@ -483,7 +485,7 @@ __device__ __forceinline__ void v5_epilogue_quant(const f32x16 (&acc)[kVTM][kVTN
                                                   const float* col_bias, int epi, int64_t M,
                                                   int64_t N, int64_t m0, int64_t n0, const Out& out,
                                                   float* st, uint16_t* st16, float* e_of) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = opaque_lane(), wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, r = lane & 31, h = lane >> 5;
   // tensor scales as the quantizer derives them from a given amax
   const uint32_t amax_bits = __float_as_uint(*out.amax_static) & 0x7FFFFFFFu;
