@@ -76,6 +76,9 @@ def parse():
     p.add_argument("--trace-command", default="", help="with --trace-json: the profiled command")
     p.add_argument("--summarize-counters", metavar="CSV",
                    help="summarize a rocprofv3 --pmc counter_collection.csv and exit (JSON)")
+    p.add_argument("--traffic-json", nargs=5, metavar=("OUT", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="write the up GEMM's HBM bytes per launch to OUT from the FETCH_SIZE and "
+                        "WRITE_SIZE counter CSVs of this script and of its --calib-copy run; exit")
     return p.parse_args()
 
 
@@ -235,6 +238,43 @@ def summarize_counters(csv_path, warmup, steps):
     return rows, headline
 
 
+def write_traffic(out, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, warmup, steps):
+    """HBM bytes per launch of the headline up GEMM from two counter runs of
+    this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled
+    by what the same counter reads for the calibration copy kernel, which
+    reads and writes 1 GiB per launch (--calib-copy)."""
+    n = 1 << 30
+
+    def copy_kib(csv_path, counter):
+        rows, _ = summarize_counters(csv_path, 0, 0)
+        r = [x for x in rows if x["kernel"] == "calib_copy_kernel"]
+        if not r or counter not in r[0]:
+            raise SystemExit(f"no calib_copy_kernel {counter} in {csv_path}")
+        return r[0][counter]
+    fetch_factor = n / 1024 / copy_kib(copy_fetch_csv, "FETCH_SIZE")
+    write_factor = n / 1024 / copy_kib(copy_write_csv, "WRITE_SIZE")
+    _, hf = summarize_counters(fetch_csv, warmup, steps)
+    _, hw = summarize_counters(write_csv, warmup, steps)
+    if not hf or not hw:
+        raise SystemExit("the counter runs do not hold the headline step's GEMM launches")
+    rd = hf["gemm_up_gelu_amax"]["FETCH_SIZE"] * 1024 * fetch_factor
+    wr = hw["gemm_up_gelu_amax"]["WRITE_SIZE"] * 1024 * write_factor
+    rd_down = hf["gemm_down"]["FETCH_SIZE"] * 1024 * fetch_factor
+    wr_down = hw["gemm_down"]["WRITE_SIZE"] * 1024 * write_factor
+    rec = {"source_hash": kernel_source_hash(), "fetch_factor": fetch_factor,
+           "write_factor": write_factor,
+           "kernels": {"gemm_nvfp4_v5_kernel": {
+               "bytes_per_launch": int(rd + wr), "read_bytes": int(rd), "written_bytes": int(wr),
+               "launch": "up projection (GELU + amax), timed steps"},
+               "gemm_nvfp4_v5_kernel (down)": {
+               "bytes_per_launch": int(rd_down + wr_down), "read_bytes": int(rd_down),
+               "written_bytes": int(wr_down), "launch": "down projection, timed steps"}}}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 def profiled_up_gemm():
     """The up GEMM's average duration over the timed steps in the committed
     kernel trace of this command, if that trace was taken on the current
@@ -315,6 +355,9 @@ def main():
         rows, headline = summarize_counters(args.summarize_counters, args.warmup, args.steps)
         print(json.dumps({"source_hash": kernel_source_hash(), "headline": headline,
                           "dispatches": rows}, indent=1))
+        return
+    if args.traffic_json:
+        write_traffic(*args.traffic_json, args.warmup, args.steps)
         return
     if args.summarize_trace:
         rows, headline = summarize_trace(args.summarize_trace, args.warmup, args.steps)
