@@ -753,9 +753,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void gemm_nvfp4_pipe_kernel(
 // Sums the slices of v5's tail tiles in split order and applies v5's epilogue
 // (same operations, same order).  Slices are in v5's accumulator order;
 // thread q of a tile takes float4 q (4 consecutive columns of one row), so
-// every slice is read contiguously.  The output amax is reduced in the
-// workgroup first: one atomic per workgroup.
-constexpr int kV5ReduceWgs = 16;            // workgroups per tail tile
+// every slice is read contiguously.  A thread issues the loads of up to 8
+// slices before it adds them (in split order), and one workgroup per 256
+// float4 of a tile gives the loads enough threads to cover their latency.
+// The output amax is reduced in the workgroup first: one atomic per
+// workgroup.
+constexpr int kV5ReduceWgs = 64;            // workgroups per tail tile
 
 __global__ __launch_bounds__(256) void v5_split_reduce_kernel(
     const float* __restrict__ part, int64_t main_tiles, int ways, const float* __restrict__ sa,
@@ -763,12 +766,14 @@ __global__ __launch_bounds__(256) void v5_split_reduce_kernel(
     int epi, uint16_t* __restrict__ y, uint32_t* __restrict__ y_amax) {
   constexpr int kQuads = kVBM * kVBN / 4;
   constexpr int kPerWg = kQuads / kV5ReduceWgs;
+  static_assert(kPerWg % 256 == 0, "whole rounds of the workgroup's threads");
   const int64_t tail = blockIdx.x / kV5ReduceWgs;
   const int64_t tiles_m = (M + kVBM - 1) / kVBM, tiles_n = (N + kVBN - 1) / kVBN;
   int64_t tm, tn;
   grouped_tile(main_tiles + tail, tiles_m, tiles_n, tm, tn);
   const float scale = (*sa) * (*sw);
   const f32x4* slices = reinterpret_cast<const f32x4*>(part) + tail * ways * (int64_t)kQuads;
+  const bool vec = N % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
   u16x2 amax = {0, 0};
   for (int q = (int)(blockIdx.x % kV5ReduceWgs) * kPerWg + threadIdx.x;
        q < (int)(blockIdx.x % kV5ReduceWgs + 1) * kPerWg; q += 256) {
@@ -779,7 +784,15 @@ __global__ __launch_bounds__(256) void v5_split_reduce_kernel(
     const int64_t row = tm * kVBM + rl, col = tn * kVBN + cl;
     if (row >= M) continue;
     f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s = 0; s < ways; ++s) sum += slices[s * (int64_t)kQuads + q];
+    for (int s0 = 0; s0 < ways; s0 += 8) {
+      f32x4 p[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (s0 + s < ways) p[s] = slices[(s0 + s) * (int64_t)kQuads + q];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (s0 + s < ways) sum += p[s];
+    }
     float v[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -788,14 +801,20 @@ __global__ __launch_bounds__(256) void v5_split_reduce_kernel(
       if (epi == 1) v[k] = gelu_erf(v[k]);
     }
     const uint32_t p01 = bf16x2_rne(v[0], v[1]), p23 = bf16x2_rne(v[2], v[3]);
-    const uint16_t hv[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
     uint16_t* dst = y + row * N + col;
+    if (vec && col + 3 < N) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{p01, p23};
+      amax = amax_bf16x2(amax_bf16x2(amax, p01), p23);
+    } else {
+      const uint16_t hv[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23,
+                              (uint16_t)(p23 >> 16)};
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (col + k < N) {
-        dst[k] = hv[k];
-        amax = max_u16x2(amax, u16x2{(unsigned short)(hv[k] & 0x7FFFu), 0});
-      }
+      for (int k = 0; k < 4; ++k)
+        if (col + k < N) {
+          dst[k] = hv[k];
+          amax = max_u16x2(amax, u16x2{(unsigned short)(hv[k] & 0x7FFFu), 0});
+        }
+    }
   }
   if (y_amax) {
     __shared__ uint32_t wave_amax[4];

@@ -411,12 +411,13 @@ _V5_SHAPES = [(300, 520, 1280), (257, 300, 1024), (64, 33, 3072), (513, 256, 256
 
 
 @pytest.mark.parametrize("M,N,K,split", [(M, N, K, split) for M, N, K in _V5_SHAPES
-                                         for split in (None, "3", "7")
+                                         for split in (None, "3", "7", "11")
                                          if split is None or int(split) <= K // 128])
 def test_gemm_v5_and_k_split(monkeypatch, M, N, K, split):
     # the direct-to-LDS kernel (K % 256 == 0) on ragged tiles, 2 to 24 stages,
-    # whole and with the tail tiles' K range split over 3 or 7 workgroups
-    # (only where the K range has at least as many 128-wide stages as ways):
+    # whole and with the tail tiles' K range split over 3, 7 or 11 workgroups
+    # (only where the K range has at least as many 128-wide stages as ways;
+    # 11 ways take the reduce kernel's slice loads in two groups of 8 and 3):
     # the splits start items at odd stages and give them odd stage counts,
     # down to one stage, which the paired scale loads treat apart
     monkeypatch.setenv("NVFP4_GEMM_KERNEL", "v5")
