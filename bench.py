@@ -151,8 +151,9 @@ def summarize_trace(csv_path, warmup, steps):
     --kernel-trace CSV of this script (launches, mean / median / min / max
     duration in us), and the headline step's two GEMMs on their own: the
     v5 kernel's launches come first in the run, as [up, down] once while the
-    step's buffers are set up, `warmup` times, then `steps` timed times, so
-    the timed up and down launches are picked by their index."""
+    step's buffers are set up, `warmup` times, then `steps` timed times (the
+    pass with per-stage events follows them), so the timed up and down
+    launches are picked by their index."""
     import csv
     groups, v5 = {}, []
     with open(csv_path, newline="") as f:
@@ -180,7 +181,7 @@ def summarize_trace(csv_path, warmup, steps):
                     "gemm_down": stats(v5[first + 1:first + 2 * steps:2]),
                     "selection": f"gemm_nvfp4_v5_kernel<false> launches {first}, {first + 2}, ... "
                                  f"(up) and {first + 1}, {first + 3}, ... (down): the {steps} timed "
-                                 f"steps after {warmup} warm-up steps and the setup call"}
+                                 f"steps after the setup call and {warmup} warm-up steps"}
     return out, headline
 
 
@@ -457,18 +458,25 @@ def main():
         if events is not None:
             events[4].record(stream)
 
+    # The timed steps: nothing but the step's own launches between the two
+    # synchronizations.  An event recorded between two kernels adds a gap of
+    # about 5 us before the next; replaying the step as a HIP graph ran each
+    # GEMM 2-3% slower, with an 8 us gap between replays.
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    # then the same number of steps again with events between the stages,
+    # for the per-stage times (not part of the headline figure)
     ev_sets = [[ev() for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
     for i in range(args.steps):
         step(ev_sets[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_per_step = wall * 1e3 / args.steps
     stage_us = {n: float(np.mean([s[j].elapsed_time(s[j + 1]) * 1e3 for s in ev_sets]))
                 for j, n in enumerate(stage_names)}
     step_ev_ms = np.array([s[0].elapsed_time(s[-1]) for s in ev_sets])
@@ -483,8 +491,8 @@ def main():
     fp8 = None if args.no_extras else fp8_section(extras)
     yardstick = None if args.no_extras else yardstick_section(extras)
 
-    # roofline of the dominant kernel: the up GEMM, timed by the step's events
-    # around its call (which also enqueues the one-word zeroing of the amax
+    # roofline of the dominant kernel: the up GEMM, timed by the events around
+    # its call in the pass with per-stage events (which also enqueues the one-word zeroing of the amax
     # the epilogue reduces into, so the figure is a little above the kernel's
     # own duration in the kernel trace)
     _progress("extra sections done; calibration kernels")
@@ -609,6 +617,8 @@ def main():
                                "quantize H -> GEMM down",
                    "tokens": TOKENS, "hidden": HIDDEN, "mlp": MLP,
                    "flop_per_step": 2 * GEMM_FLOP, "parallelism": "single GPU"},
+        "timing": "wall clock over the timed steps between two synchronizations, no events "
+                  "between the stages; stages_us from as many further steps with events",
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
         "step_ms_events": step_pct,
         "weight_quantize_us": round(wquant_us, 2),
