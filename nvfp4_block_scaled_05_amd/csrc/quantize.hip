@@ -268,9 +268,15 @@ __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
 // partials already published and reads only the ranges of the workgroups
 // whose partial is missing (slower, but the same value), so the kernel always
 // completes and always gives the same bytes.
+// The kernel is instantiated for three footprints, R 16-element blocks per
+// thread in registers and L more in LDS: <9, 4> (13 blocks: up to 13,312 per
+// workgroup, 54.5 M elements on 256 compute units; 4 * 32 B * 1024 = 128 KB
+// of LDS), <4, 0> and <2, 0>.  A call takes the smallest that holds its
+// range, so a mid-size tensor does not issue the loads of the large
+// footprint (clamped to its last block) for nothing.
 static constexpr int kResThreads = 1024;
-static constexpr int kResR = 9;   // 16-element blocks per thread held in registers
-static constexpr int kResL = 4;   // ... and in LDS (4 * 32 B * 1024 = 128 KB)
+static constexpr int kResR = 9;   // the large footprint: blocks per thread in registers
+static constexpr int kResL = 4;   // ... and in LDS
 static constexpr uint64_t kResWaitTicks = 20000;   // 200 us of the 100 MHz real-time counter
 
 // Workspace words of the arrival.  Workgroups are dealt to kXcds groups
@@ -300,12 +306,21 @@ __device__ __forceinline__ uint64_t* res_u64(uint32_t* sync, int word) {
   return reinterpret_cast<uint64_t*>(sync + word);
 }
 
+// One 16-byte global load per lane straight into LDS (lane L's bytes at
+// byte 16 L of the wave's destination).  A plain device function: called in
+// the body of a kernel template, the builtin made the host-side
+// instantiation fail silently and the kernel's launch stub was never emitted.
+__device__ __forceinline__ void load16_to_lds(const u32x4* src, u32x4* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+template <int R, int L>
 __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(
     const u32x4* __restrict__ x, uint32_t nblocks, uint32_t chunk, u32x2* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tensor_scale, int32_t* __restrict__ dev_status,
     uint32_t* __restrict__ sync, uint64_t wait_ticks) {
-  constexpr int T = kResThreads, NW = T / 64, R = kResR, L = kResL;
-  __shared__ u32x4 stage[NW][L][128];   // wave w, slot s: 64 blocks = 128 words
+  constexpr int T = kResThreads, NW = T / 64;
+  __shared__ u32x4 stage[NW][L > 0 ? L : 1][128];   // wave w, slot s: 64 blocks = 128 words
   __shared__ float e_of[128];           // encode factor of every scale byte
   __shared__ uint32_t red[NW];
   __shared__ uint32_t shared_ok, shared_tag;
@@ -324,8 +339,7 @@ __global__ __launch_bounds__(kResThreads) void quantize_resident_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t word = 2 * blk0 + (uint32_t)(64 * i + lane);
-      __builtin_amdgcn_global_load_lds(x + (word < 2 * last + 1 ? word : 2 * last + 1),
-                                       &stage[wave][s][64 * i], 16, 0, 0);
+      load16_to_lds(x + (word < 2 * last + 1 ? word : 2 * last + 1), &stage[wave][s][64 * i]);
     }
   }
   u32x4 a[R], b[R];
@@ -541,13 +555,14 @@ int amax_partial_count(int64_t numel) {
 
 // The single-pass kernel is used when the amax is computed here, the tensor
 // fits on chip (at most units * (R + L) * 1024 blocks of 16: 109 MB of bf16 on
-// 256 compute units), it is at least kResMinElems elements (below that the
-// two launches of the two-pass kernels cost no more: both are about 15 us
-// there), and the workspace holds the counters, the release words and one
-// slot per compute unit.  NVFP4_QUANT_KERNEL=twopass turns it off, =resident
-// lifts the size floor.  One launch per call: the arrival words are never
-// cleared (see above), so no clearing kernel runs before it.
-static constexpr int64_t kResMinElems = (int64_t)3 << 23;   // 25.2 M elements
+// 256 compute units), it is above the one-launch kernel's size (from 0.4 M to
+// 14 M elements the single pass in its small footprints takes about 14 us a
+// call and the two passes about 16.5), and the workspace holds the counters,
+// the release words and one slot per compute unit.  NVFP4_QUANT_KERNEL=twopass
+// turns it off, =resident also takes it for the smallest tensors.  One launch
+// per call: the arrival words are never cleared (see above), so no clearing
+// kernel runs before it.
+static constexpr int64_t kResMinElems = kSmallMaxElems + 1;
 
 static bool try_resident(const u32x4* xv, int64_t nblocks, u32x2* codes, uint8_t* scales,
                          float* tensor_scale, uint32_t* workspace, size_t workspace_bytes,
@@ -566,8 +581,15 @@ static bool try_resident(const u32x4* xv, int64_t nblocks, u32x2* codes, uint8_t
   // partials' ranges themselves)
   uint64_t wait_ticks = kResWaitTicks;
   if (const char* w = getenv("NVFP4_QUANT_WAIT_TICKS")) wait_ticks = strtoull(w, nullptr, 10);
-  hipLaunchKernelGGL(quantize_resident_kernel, dim3(units), dim3(kResThreads), 0, stream, xv, nb,
-                     chunk, codes, scales, tensor_scale, dev_status, workspace, wait_ticks);
+  if (chunk <= 2u * kResThreads)
+    quantize_resident_kernel<2, 0><<<dim3(units), dim3(kResThreads), 0, stream>>>(
+        xv, nb, chunk, codes, scales, tensor_scale, dev_status, workspace, wait_ticks);
+  else if (chunk <= 4u * kResThreads)
+    quantize_resident_kernel<4, 0><<<dim3(units), dim3(kResThreads), 0, stream>>>(
+        xv, nb, chunk, codes, scales, tensor_scale, dev_status, workspace, wait_ticks);
+  else
+    quantize_resident_kernel<kResR, kResL><<<dim3(units), dim3(kResThreads), 0, stream>>>(
+        xv, nb, chunk, codes, scales, tensor_scale, dev_status, workspace, wait_ticks);
   return true;
 }
 

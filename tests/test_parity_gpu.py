@@ -145,6 +145,22 @@ def test_quantize_single_pass_capacity_edge(extra_rows):
     assert q.tensor_scale.cpu().numpy().view(np.uint32)[0] == np.float32(ref.tensor_scale).view(np.uint32)
 
 
+@pytest.mark.parametrize("blocks_per_thread,extra", [(2, 0), (2, 1), (4, 0), (4, 1)])
+def test_quantize_single_pass_footprint_edges(blocks_per_thread, extra):
+    # the single-pass kernel comes in three footprints (2, 4 and 13 blocks of
+    # 16 per thread); a call takes the smallest whose 1024 threads hold its
+    # workgroup's range.  At each edge, and one row past it (the next
+    # footprint), the whole tensor against the oracle
+    import torch
+    units = torch.cuda.get_device_properties(0).multi_processor_count
+    cols = 3072
+    rows = blocks_per_thread * 1024 * units * 16 // cols + extra
+    chunk = -(-(rows * cols // 16) // units)
+    assert (chunk <= blocks_per_thread * 1024) == (extra == 0)
+    bits = W.random_matrix(40 + 2 * blocks_per_thread + extra, (rows, cols), "outliers")
+    check_quantize(bits, label=f"[{rows},{cols}] chunk {chunk}")
+
+
 @functools.lru_cache(maxsize=None)
 def _mlp():
     return W.mlp_2048()
