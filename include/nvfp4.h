@@ -122,7 +122,8 @@ size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
  *   else e_b = 1 / (S_b * s_dec), code = sign | E2M1(|x| * e_b), nearest-even,
  *     saturating at 6.
  * Deterministic: the same input gives the same bytes on every call.
- * When the amax is computed here and the tensor has at least 25.2 M
+ * rows == 0: nothing is launched and *tensor_scale is not written.
+ * When the amax is computed here and the tensor has more than 262,144
  * elements and fits on chip (at most 212,992 elements per compute unit: 54.5 M
  * elements, 109 MB of bf16, on 256 units), it is read from HBM once: one
  * workgroup per compute unit holds its share on chip while the amax is
@@ -241,7 +242,8 @@ int nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_t
  *   y_codes          out [M, N/2] bytes, 8-byte aligned.
  *   y_scales         out [M, N/16] E4M3 bytes.
  *   y_tensor_scale   out, 1 float (s_dec).
- * Tiles are computed whole (no K split).
+ * Tiles are computed whole (no K split).  M == 0 or N == 0: nothing is
+ * launched and *y_tensor_scale is not written (as nvfp4_quantize with no rows).
  */
 int nvfp4_gemm_quantized(const uint8_t* a_codes, const uint8_t* a_scales,
                          const float* a_tensor_scale, const uint8_t* w_codes,

@@ -247,6 +247,27 @@ def test_quantize_empty_rows():
     assert q.codes.shape == (0, 32)
 
 
+@pytest.mark.parametrize("which", ["a", "w"])
+def test_gemm_empty_operand(which):
+    # an operand with no rows: an empty output, no kernel reads the other
+    # operand, and the output amax (the max over no values) is written as 0,
+    # for the bf16 and the NVFP4-output GEMMs alike
+    import torch
+    K = 1024
+    empty = nv.quantize(torch.empty((0, K), dtype=torch.bfloat16, device="cuda"))
+    full, _ = check_quantize(W.random_matrix(17, (96, K), "t3"), label="operand")
+    a, w = (empty, full) if which == "a" else (full, empty)
+    amax = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    y = nv.gemm(a, w, epilogue="gelu", y_amax=amax)
+    _sync()
+    assert tuple(y.shape) == ((0, 96) if which == "a" else (96, 0))
+    assert amax.item() == 0.0
+    if which == "a":
+        q = nv.gemm_quantized(a, w, torch.ones((1,), dtype=torch.float32, device="cuda"))
+        _sync()
+        assert tuple(q.codes.shape) == (0, 48)
+
+
 def test_quantize_deterministic(quant_kernel):
     bits = W.random_matrix(9, (1000, 3072), "outliers")
     x = to_dev(bits)
