@@ -615,8 +615,11 @@ __global__ __launch_bounds__(kDNT, 1) void gemm_fp8_dma_kernel(
 // Sums the slices of the tail tiles in split order and applies the epilogue
 // of the whole tiles (same operations, same order).  Slices are in the
 // accumulator order of gemm_fp8_dma_kernel; thread q of a tile takes float4 q
-// (4 consecutive columns of one row), so every slice is read contiguously.
-constexpr int kFp8ReduceWgs = 16;             // workgroups per tail tile
+// (4 consecutive columns of one row), so every slice is read contiguously.  A
+// thread issues the loads of up to 8 slices before it adds them (in split
+// order), with one workgroup per 256 float4 of a tile, and interior rows
+// store their 4 outputs at once.
+constexpr int kFp8ReduceWgs = 64;             // workgroups per tail tile
 
 __global__ __launch_bounds__(256) void fp8_split_reduce_kernel(
     const float* __restrict__ part, int64_t main_tiles, int ways, const float* __restrict__ da,
@@ -624,11 +627,13 @@ __global__ __launch_bounds__(256) void fp8_split_reduce_kernel(
     uint16_t* __restrict__ y) {
   constexpr int kQuads = kDBM * kDBN / 4;       // float4 per slice
   constexpr int kPerWg = kQuads / kFp8ReduceWgs;
+  static_assert(kPerWg % 256 == 0, "whole rounds of the workgroup's threads");
   const int64_t tail = blockIdx.x / kFp8ReduceWgs;
   const int64_t tiles_m = (M + kDBM - 1) / kDBM, tiles_n = (N + kDBN - 1) / kDBN;
   int64_t tm, tn;
   grouped_tile(main_tiles + tail, tiles_m, tiles_n, tm, tn);
   const f32x4* slices = reinterpret_cast<const f32x4*>(part) + tail * ways * (int64_t)kQuads;
+  const bool vec = N % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
   for (int q = (int)(blockIdx.x % kFp8ReduceWgs) * kPerWg + threadIdx.x;
        q < (int)(blockIdx.x % kFp8ReduceWgs + 1) * kPerWg; q += 256) {
     // q = (((wave * 4 + i) * 4 + j) * 64 + lane) * 4 + g
@@ -638,7 +643,15 @@ __global__ __launch_bounds__(256) void fp8_split_reduce_kernel(
     const int64_t row = tm * kDBM + rl, col = tn * kDBN + cl;
     if (row >= M) continue;
     f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s = 0; s < ways; ++s) sum += slices[s * (int64_t)kQuads + q];
+    for (int s0 = 0; s0 < ways; s0 += 8) {
+      f32x4 p[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (s0 + s < ways) p[s] = slices[(s0 + s) * (int64_t)kQuads + q];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (s0 + s < ways) sum += p[s];
+    }
     const float rs = da[row];
     float v[4];
 #pragma unroll
@@ -650,11 +663,16 @@ __global__ __launch_bounds__(256) void fp8_split_reduce_kernel(
       if (epi == 1) v[k] = gelu_erf(v[k]);
     }
     const uint32_t p01 = bf16x2_rne(v[0], v[1]), p23 = bf16x2_rne(v[2], v[3]);
-    const uint16_t hv[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
     uint16_t* dst = y + row * N + col;
+    if (vec && col + 3 < N) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{p01, p23};
+    } else {
+      const uint16_t hv[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23,
+                              (uint16_t)(p23 >> 16)};
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (col + k < N) dst[k] = hv[k];
+      for (int k = 0; k < 4; ++k)
+        if (col + k < N) dst[k] = hv[k];
+    }
   }
 }
 

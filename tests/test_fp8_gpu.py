@@ -136,10 +136,11 @@ def test_fp8_gemm_mlp_down_sampled_rows():
     _close(y[rows], ref, "fp8 down sampled rows")
 
 
-@pytest.mark.parametrize("ways", [2, 3, 7])
+@pytest.mark.parametrize("ways", [2, 3, 7, 11])
 @pytest.mark.parametrize("M,N,K", [(600, 520, 1280), (257, 300, 2048)])
 def test_fp8_gemm_split_k(M, N, K, ways, monkeypatch):
     # the tail tiles split over K (forced), partial sums added in split order
+    # (more than 8 ways: the reduce kernel loads the slices in groups of 8)
     monkeypatch.setenv("NVFP4_FP8_GEMM_SPLIT", str(ways))
     a_bits = W.random_matrix(M * 3 + K, (M, K), "t3")
     w_bits = W.random_matrix(N * 3 + K, (N, K), "normal", 0.02)
