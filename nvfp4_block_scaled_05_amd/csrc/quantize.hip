@@ -555,9 +555,10 @@ int amax_partial_count(int64_t numel) {
 
 // The single-pass kernel is used when the amax is computed here, the tensor
 // fits on chip (at most units * (R + L) * 1024 blocks of 16: 109 MB of bf16 on
-// 256 compute units), it is above the one-launch kernel's size (from 0.4 M to
-// 14 M elements the single pass in its small footprints takes about 14 us a
-// call and the two passes about 16.5), and the workspace holds the counters,
+// 256 compute units), it is above the one-launch kernel's size (back to back
+// through the C ABI the single pass in its small footprints takes 7.6 us a
+// call at 0.5-1 M elements and 13 us at 14 M, the two passes 8.5 and 15), and
+// the workspace holds the counters,
 // the release words and one slot per compute unit.  NVFP4_QUANT_KERNEL=twopass
 // turns it off, =resident also takes it for the smallest tensors.  One launch
 // per call: the arrival words are never cleared (see above), so no clearing
