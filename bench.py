@@ -185,6 +185,11 @@ def summarize_trace(csv_path, warmup, steps):
     return out, headline
 
 
+LIBRARY_KERNEL_PREFIXES = ("gemm_nvfp4", "gemm_fp8", "gemm_bf16", "gemv_bf16", "quantize_",
+                           "amax_partial", "dequantize", "v5_split_reduce", "split_reduce",
+                           "fp8_", "zero_", "calib_")
+
+
 def print_trace_summary(rows, headline, source_hash, command, json_path=None):
     print("| kernel | workgroups | launches | average us | median us | min us | max us |")
     print("|---|---|---|---|---|---|---|")
@@ -200,9 +205,12 @@ def print_trace_summary(rows, headline, source_hash, command, json_path=None):
             print(f"| {k} | {r['launches']} | {r['avg_us']} | {r['median_us']} | {r['min_us']} | "
                   f"{r['max_us']} |")
     if json_path:
+        # the library's own kernels only (torch's fills, casts and the
+        # yardstick GEMMs stay in the printed table)
+        own = [r for r in rows if r["kernel"].startswith(LIBRARY_KERNEL_PREFIXES)]
         with open(json_path, "w") as f:
             json.dump({"source_hash": source_hash, "command": command, "headline": headline,
-                       "dispatches": rows}, f, indent=1)
+                       "dispatches": own}, f, indent=1)
             f.write("\n")
 
 
