@@ -211,18 +211,12 @@ __device__ __forceinline__ void v5_decode(const V5Packed& p, V5Ops& o) {
   }
 }
 
-// The 16 MFMAs of a step in serpentine order (j descending on odd i): each
-// A fragment change keeps the W operand of the MFMA before it, so fewer
-// operand bits switch between consecutive products on this power-limited
-// part.  Every accumulator still sums its steps in K order: the same bits.
 __device__ __forceinline__ void v5_mfma(const V5Ops& o, f32x16 (&acc)[kVTM][kVTN]) {
 #pragma unroll
   for (int i = 0; i < kVTM; ++i)
 #pragma unroll
-    for (int jj = 0; jj < kVTN; ++jj) {
-      const int j = (i & 1) ? kVTN - 1 - jj : jj;
+    for (int j = 0; j < kVTN; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.v[4 + j], o.v[i], acc[i][j], 0, 0, 0);
-    }
 }
 
 // MFMAs of step S-1 (in `cur`) interleaved with the decode of step S (into
