@@ -23,13 +23,30 @@ __all__ = ["Nvfp4Tensor", "Fp8Tensor", "Nvfp4Error", "load", "abi_version", "sta
            "fp8_quantize", "fp8_gemm", "fp8_gemm_workspace"]
 
 
+_TORCH = None
+_RAW_STREAM = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _TORCH
+    if _TORCH is None:
+        import torch
+        _TORCH = torch
+    return _TORCH
 
 
 def _stream():
-    return _torch().cuda.current_stream().cuda_stream
+    """The current HIP stream of the current device, as a pointer-sized int.
+    torch's own raw-stream getter when it has one: building the Stream object
+    of torch.cuda.current_stream() costs about 3 us a call, a large part of a
+    small call's host time."""
+    global _RAW_STREAM
+    torch = _torch()
+    if _RAW_STREAM is None:
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _RAW_STREAM:
+        return _RAW_STREAM(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _ptr(t):
@@ -49,7 +66,7 @@ def _tensor(t, name, dtype, shape=None, min_numel=1):
         raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous (got strides {tuple(t.stride())})")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != tuple(shape):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
     if shape is None and t.numel() < min_numel:
         raise ValueError(f"{name}: needs at least {min_numel} element(s)")

@@ -247,6 +247,24 @@ def test_quantize_empty_rows():
     assert q.codes.shape == (0, 32)
 
 
+def test_binding_stream_is_torch_current_stream():
+    # the binding enqueues on the stream torch.cuda.current_stream() names,
+    # on the default stream and inside a side-stream context, and work
+    # enqueued there is ordered with torch's own work on that stream
+    import torch
+    from nvfp4_block_scaled_05_amd import _stream
+    assert _stream() == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    bits = W.random_matrix(23, (64, 256), "normal")
+    ref = o_quantize(bits)
+    with torch.cuda.stream(side):
+        assert _stream() == side.cuda_stream != torch.cuda.default_stream().cuda_stream
+        x = to_dev(bits)
+        q = nv.quantize(x)
+    side.synchronize()
+    assert_quant_equal(q, ref, "side stream")
+
+
 @pytest.mark.parametrize("which", ["a", "w"])
 def test_gemm_empty_operand(which):
     # an operand with no rows: an empty output, no kernel reads the other
